@@ -1,0 +1,322 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: hand-derived worked
+examples, the x86 F16C instruction, exact-rational brute force, invariants of
+the quantizer, and closed forms of the matmul.
+"""
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from tests import exact
+from weight_only_bit_block_amd import inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def _read_golden(name):
+    lines = [l.strip() for l in open(os.path.join(HERE, "golden", name)) if l.strip()]
+    data = [l for l in lines if not l.startswith("#")]
+    w_mult = [float(v) for v in data[0].split()]
+    codes = [int(v) for v in data[1].split()]
+    scale = int(data[2], 16)
+    packed = bytes(int(v, 16) for v in data[3].split())
+    return w_mult, codes, scale, packed
+
+
+# ---------------------------------------------------------------- fp16 rounding
+
+def test_f16_exhaustive_vs_f16c(oracle_mod, tmp_path):
+    """All 2^32 binary32 patterns round to the same binary16 as vcvtps2ph (RNE)."""
+    exe = str(tmp_path / "f16ex")
+    src = os.path.join(HERE, "c", "f16_exhaustive.c")
+    odir = os.path.join(ROOT, "oracle")
+    subprocess.check_call(["gcc", "-O2", "-mf16c", "-fopenmp", "-o", exe, src,
+                           "-L", odir, "-loracle", "-Wl,-rpath," + odir])
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "mismatches 0 nan_mismatches 0" in out.stdout
+
+
+def _f16_grid():
+    """Every finite binary16 value, the midpoints between neighbours, and the
+    binary32 neighbours of those midpoints (all exactly representable in fp32)."""
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    mids = (v[:-1] + v[1:]) / 2                       # exact in fp32 (<= 12 bits)
+    top = 65504.0 + 16.0                              # midpoint to the overflow threshold
+    pts = np.concatenate([v, mids, [top]]).astype(np.float32)
+    up = np.nextafter(pts, np.float32(np.inf))
+    dn = np.nextafter(pts, np.float32(0))
+    allp = np.concatenate([pts, up, dn])
+    return np.concatenate([allp, -allp]).astype(np.float32)
+
+
+def test_f16_nearest_ties_even(oracle_mod):
+    """The result is a nearest binary16, ties to even, overflow to inf (by definition)."""
+    x = _f16_grid()
+    bits = oracle_mod.f16_bits(x)
+    finite = np.arange(0, 0x7C00, dtype=np.uint16)
+    fv = finite.view(np.float16).astype(np.float64)
+    ax = np.abs(x.astype(np.float64))
+    got_mag = bits & 0x7FFF
+    # overflow region: |x| >= 65520 must give inf
+    ovf = ax >= 65520.0
+    assert np.all(got_mag[ovf] == 0x7C00)
+    assert np.all(got_mag[~ovf] < 0x7C00)
+    nz = ~ovf
+    g = got_mag[nz]
+    gv = fv[g]
+    a = ax[nz]
+    err = np.abs(gv - a)
+    # neighbours of the chosen value
+    lo_v = fv[np.maximum(g.astype(np.int64) - 1, 0)]
+    hi_v = np.where(g < 0x7BFF, fv[np.minimum(g.astype(np.int64) + 1, 0x7BFF)], np.inf)
+    assert np.all(err <= np.abs(lo_v - a))
+    assert np.all(err <= np.abs(hi_v - a))
+    tie = (np.abs(lo_v - a) == err) & (g > 0) | (np.abs(hi_v - a) == err)
+    assert np.all((g[tie] & 1) == 0)                  # ties go to the even mantissa
+    # sign is kept (including -0)
+    assert np.all((bits >> 15) == (np.signbit(x)).astype(np.uint16))
+
+
+def test_f16_roundtrip_values(oracle_mod):
+    h = np.arange(0, 0x10000, dtype=np.uint16)
+    finite = (h & 0x7C00) != 0x7C00
+    ref = h[finite].view(np.float16).astype(np.float64)
+    got = oracle_mod.f64_from_f16_bits(h[finite])
+    assert np.array_equal(got, ref)
+    # every finite binary16 value converts back to its own bits
+    back = oracle_mod.f16_bits(got.astype(np.float32))
+    assert np.array_equal(back, h[finite])
+
+
+# ---------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("name,bits,unit", [
+    ("int4_block_worked_example.txt", 4, 2.0 ** -7),
+    ("int8_block_worked_example.txt", 8, 2.0 ** -8),
+])
+def test_worked_examples(oracle_mod, name, bits, unit):
+    w_mult, codes, scale, packed = _read_golden(name)
+    w = (np.array(w_mult, dtype=np.float64) * unit).astype(np.float32)[None, :]
+    q, s = oracle_mod.quantize(w, bits)
+    assert int(s[0, 0]) == scale
+    assert bytes(q[0]) == packed
+    assert list(oracle_mod.decode(q, 32, bits)[0]) == codes
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_block(oracle_mod, bits):
+    w = np.zeros((3, 64), dtype=np.float32)
+    w[1, 40] = 0.5            # second block of row 1 is non-zero
+    q, s = oracle_mod.quantize(w, bits)
+    assert s[0].tolist() == [0, 0] and s[2].tolist() == [0, 0] and s[1, 0] == 0
+    assert s[1, 1] != 0
+    assert not q[0].any() and not q[2].any()
+    half = q.shape[1] // 2
+    assert not q[1, :half].any()
+
+
+def test_non_dyadic_scale(oracle_mod):
+    """A block whose only non-zero is 1.0: s32 = fl32(1/7), s16 = 0x3092, code 7."""
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, 5] = 1.0
+    q, s = oracle_mod.quantize(w, 4)
+    assert int(s[0, 0]) == 0x3092
+    assert exact.f16_value(0x3092) == Fraction(585, 4096)    # 0.142822265625
+    codes = oracle_mod.decode(q, 32, 4)[0]
+    assert codes[5] == 7 and np.count_nonzero(codes) == 1
+    wh = oracle_mod.dequant(q, s, 32, 4)[0, 5]
+    assert wh == 0.999755859375
+
+
+def _crafted_blocks(bits):
+    """Blocks whose scale is an exact binary16 value and whose ratios w/s hit
+    exact half-integers and their binary32 neighbours."""
+    Q = 7 if bits == 4 else 127
+    rows = []
+    rng = inputs.generator((99, bits))
+    for s_bits in [0x2000, 0x1C00, 0x3092, 0x2155, 0x0001, 0x03FF, 0x0400, 0x1FFF, 0x5000]:
+        s = float(np.uint16(s_bits).view(np.float16))
+        blk = np.empty(32, dtype=np.float32)
+        blk[0] = np.float32(Q * s)
+        halves = (np.arange(-Q, Q) + 0.5)
+        pick = rng.choice(halves, 31)
+        vals = (pick * s).astype(np.float32)
+        # nudge a third of them one binary32 ulp either way
+        nud = rng.integers(-1, 2, 31)
+        vals = np.where(nud > 0, np.nextafter(vals, np.float32(np.inf)), vals)
+        vals = np.where(nud < 0, np.nextafter(vals, np.float32(-np.inf)), vals)
+        blk[1:] = vals
+        rows.append(blk)
+    # plain Gaussian blocks at several magnitudes, incl. binary16-subnormal scales
+    for sig in [0.02, 1.0, 3e-3, 1e-6, 3e-8, 100.0]:
+        rows.append(rng.standard_normal(32).astype(np.float32) * np.float32(sig))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_vs_exact_rational(oracle_mod, bits):
+    """Scale bits and every code equal an exact-rational evaluation of the rule."""
+    w = _crafted_blocks(bits)
+    q, s = oracle_mod.quantize(w, bits)
+    codes = oracle_mod.decode(q, 32, bits)
+    for i in range(w.shape[0]):
+        want_codes, want_s = exact.quantize_block_exact(w[i], bits)
+        assert exact.f16_value(int(s[i, 0])) == want_s, i
+        assert codes[i].tolist() == want_codes, i
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_invariants(oracle_mod, bits):
+    """On N(0, 0.02) weights: every non-zero block reaches +-Q, codes stay in
+    [-Q, Q], the reconstruction error is at most half a scale, and packing the
+    dequantized weights again reproduces the same bytes."""
+    Q = 7 if bits == 4 else 127
+    w = inputs.normal((512, 1024), seed=(7, bits), sigma=0.02)
+    q, s = oracle_mod.quantize(w, bits)
+    codes = oracle_mod.decode(q, 1024, bits).astype(np.int64).reshape(512, 32, 32)
+    assert np.all(np.abs(codes).max(axis=2) == Q)
+    assert codes.min() >= -Q and codes.max() <= Q
+    wh = oracle_mod.dequant(q, s, 1024, bits)
+    sv = oracle_mod.f64_from_f16_bits(s)
+    err = np.abs(w.astype(np.float64) - wh).reshape(512, 32, 32)
+    assert np.all(err <= sv[:, :, None] / 2)
+    q2, s2 = oracle_mod.quantize(wh.astype(np.float32), bits)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_decode_table(oracle_mod):
+    """All 256 bytes decode to (low nibble, high nibble) two's-complement pairs
+    (int4) and to the two's-complement byte (int8); 0x88 and 0x80 give -8 and -128."""
+    allb = np.arange(256, dtype=np.uint8)
+    q4 = allb.reshape(16, 16)
+    c4 = oracle_mod.decode(q4, 32, 4).reshape(-1)
+    for i, b in enumerate(allb):
+        assert c4[2 * i] == exact.signed_nibble(int(b) & 0xF)
+        assert c4[2 * i + 1] == exact.signed_nibble(int(b) >> 4)
+    q8 = allb.reshape(8, 32)
+    c8 = oracle_mod.decode(q8, 32, 8).reshape(-1)
+    assert np.array_equal(c8, allb.view(np.int8))
+    assert oracle_mod.decode(np.full((1, 16), 0x88, np.uint8), 32, 4).tolist() == [[-8] * 32]
+    assert oracle_mod.decode(np.full((1, 32), 0x80, np.uint8), 32, 8).tolist() == [[-128] * 32]
+
+
+# ---------------------------------------------------------------- matmul
+
+def _exact_dequant(q, s, K, bits):
+    """Exact dequantized weights as Fractions, decoding bytes independently."""
+    N = q.shape[0]
+    out = []
+    for n in range(N):
+        row = []
+        for k in range(K):
+            if bits == 4:
+                byte = int(q[n, k // 2])
+                t = exact.signed_nibble(byte & 0xF if k % 2 == 0 else byte >> 4)
+            else:
+                t = int(np.uint8(q[n, k]).view(np.int8))
+            row.append(t * exact.f16_value(int(s[n, k // 32])))
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (2, 64, 3), (3, 96, 5), (1, 96, 4), (3, 32, 2)])
+def test_matmul_exact_rational(oracle_mod, bits, M, K, N):
+    """y equals the exact rational sum up to the binary64 summation bound."""
+    rng = inputs.generator((11, bits, M, K, N))
+    x = (rng.integers(-2 ** 12, 2 ** 12, (M, K)) * 2.0 ** -9).astype(np.float32)
+    x[0, 0] = np.float32(1.0 + 2.0 ** -23)          # a full-width binary32 significand
+    w = inputs.normal((N, K), seed=(12, bits, M, K, N), sigma=0.02)
+    q, s = oracle_mod.quantize(w, bits)
+    y, B = oracle_mod.matmul(x, q, s, bits)
+    wh = _exact_dequant(q, s, K, bits)
+    for m in range(M):
+        for n in range(N):
+            ye = sum(Fraction(float(x[m, k])) * wh[n][k] for k in range(K))
+            be = sum(abs(Fraction(float(x[m, k])) * wh[n][k]) for k in range(K))
+            assert abs(Fraction(y[m, n]) - ye) <= (K - 1) * Fraction(1, 2 ** 53) * be
+            assert abs(Fraction(B[m, n]) - be) <= K * Fraction(1, 2 ** 53) * be
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matmul_one_hot_readout(oracle_mod, bits):
+    """x = e_k reads column k of the dequantized weights exactly, for every k."""
+    K, N = 96, 7
+    w = inputs.normal((N, K), seed=(13, bits), sigma=0.02)
+    w[:, 32:64] *= 50                                 # distinct scales per block
+    q, s = oracle_mod.quantize(w, bits)
+    x = np.eye(K, dtype=np.float32)
+    y, _ = oracle_mod.matmul(x, q, s, bits)
+    wh = _exact_dequant(q, s, K, bits)
+    for k in range(K):
+        for n in range(N):
+            assert Fraction(y[k, n]) == wh[n][k]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matmul_zero_scale_row_and_signs(oracle_mod, bits):
+    K, N, M = 64, 5, 3
+    w = inputs.normal((N, K), seed=(14, bits), sigma=0.02)
+    q, s = oracle_mod.quantize(w, bits)
+    s0 = s.copy()
+    s0[2, :] = 0                                      # codes stay non-zero
+    x = inputs.normal((M, K), seed=(15, bits))
+    y, _ = oracle_mod.matmul(x, q, s0, bits)
+    assert np.all(y[:, 2] == 0)
+    y1, _ = oracle_mod.matmul(x, q, s, bits)
+    yn, _ = oracle_mod.matmul(-x, q, s, bits)
+    y8, _ = oracle_mod.matmul(x * np.float32(8), q, s, bits)
+    assert np.array_equal(yn, -y1)
+    assert np.array_equal(y8, 8 * y1)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matmul_linearity_and_library(oracle_mod, bits):
+    """Linear in x within the binary64 bound, and equal to a library fp64 matmul
+    over the dequantized weights within the same bound."""
+    K, N, M = 256, 33, 4
+    w = inputs.normal((N, K), seed=(16, bits), sigma=0.02)
+    q, s = oracle_mod.quantize(w, bits)
+    x1 = inputs.normal((M, K), seed=(17, bits))
+    x2 = inputs.normal((M, K), seed=(18, bits))
+    y1, b1 = oracle_mod.matmul(x1, q, s, bits)
+    y2, b2 = oracle_mod.matmul(x2, q, s, bits)
+    x12 = (x1.astype(np.float64) * 0.5 + x2.astype(np.float64) * 0.25).astype(np.float32)
+    y12, b12 = oracle_mod.matmul(x12, q, s, bits)
+    # x12 itself is rounded to fp32: compare with the exact image of that rounded input
+    wh = oracle_mod.dequant(q, s, K, bits)
+    ylib = x12.astype(np.float64) @ wh.T
+    bound = 2 * K * 2.0 ** -53 * b12
+    assert np.all(np.abs(y12 - ylib) <= bound)
+    lin = 0.5 * y1 + 0.25 * y2
+    rnd = np.abs(x12.astype(np.float64) - (x1.astype(np.float64) * 0.5 + x2.astype(np.float64) * 0.25))
+    assert np.all(np.abs(y12 - lin) <= bound + 2 * K * 2.0 ** -53 * (b1 + b2) + rnd @ np.abs(wh).T)
+
+
+def test_matmul_x16_diagnostic(oracle_mod):
+    """The fp16-activation reference equals the matmul of binary16-rounded x."""
+    K, N, M = 128, 9, 3
+    w = inputs.normal((N, K), seed=(19,), sigma=0.02)
+    q, s = oracle_mod.quantize(w, 4)
+    x = inputs.normal((M, K), seed=(20,)) * np.float32(3.0)
+    y16, _ = oracle_mod.matmul(x, q, s, 4, x16=True)
+    xr = x.astype(np.float16).astype(np.float32)       # library rounding (RNE)
+    yr, _ = oracle_mod.matmul(xr, q, s, 4)
+    assert np.array_equal(y16, yr)
+
+
+def test_threads_do_not_change_results(oracle_mod):
+    K, N, M = 512, 64, 2
+    w = inputs.normal((N, K), seed=(21,), sigma=0.02)
+    q, s = oracle_mod.quantize(w, 4)
+    x = inputs.normal((M, K), seed=(22,))
+    y1, _ = oracle_mod.matmul(x, q, s, 4, threads=1)
+    y4, _ = oracle_mod.matmul(x, q, s, 4, threads=4)
+    assert np.array_equal(y1, y4)
