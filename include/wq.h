@@ -1,0 +1,164 @@
+/*
+ * wq.h -- weight-only block-32 int4/int8 matmul for AMD MI355X (gfx950).
+ *
+ * The operation (TinyMOSS-Diarize devpost page, "How we built it": strictly
+ * weight-only kernels, FP32 activations, dequantization fused into the matmul,
+ * no dequantized weight tensor ever materialized; moss-transcribe-diarize-litert
+ * card, "v2 decoder": int4 block-32; soniqo MOSS guide RU, implementation notes:
+ * symmetric linear INT8 block-32):
+ *
+ *     y[m,n] = sum_b s[n,b] * sum_{k in block b} q[n,k] * x[m,k]
+ *
+ * Layouts (one canonical layout, all row-major and contiguous):
+ *   x       fp32  [M][K]
+ *   y       fp32  [M][N]            (overwritten; no bias, no accumulate)
+ *   q int4  uint8 [N][K/2]          two codes per byte, low nibble = even k,
+ *                                   two's complement, codes in [-8, 7]
+ *   q int8  int8  [N][K]            two's complement, codes in [-128, 127]
+ *   scales  binary16 bits [N][K/32] one scale per 32 consecutive k
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers on the current HIP device, owned by the
+ *     caller; the library allocates nothing and keeps no state.
+ *   - Arguments are validated on the host before any launch; a non-zero
+ *     wq_status is returned and nothing is launched. Requirements: bits in
+ *     {4, 8}; K > 0 and K % 32 == 0; N >= 0; M >= 0; non-null pointers for
+ *     non-empty calls; x, y, q, scales 16-byte aligned. y must not alias an
+ *     input.
+ *   - Empty calls (M == 0 or N == 0) return WQ_OK without launching.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); a
+ *     launch error is reported as WQ_ERR_HIP. There is no implicit sync.
+ *   - Results are deterministic: no atomics, a fixed reduction order.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum wq_status {
+    WQ_OK = 0,
+    WQ_ERR_NULL = 1,      /* a required pointer is null */
+    WQ_ERR_SHAPE = 2,     /* K <= 0, K % 32 != 0, negative M or N, or too large */
+    WQ_ERR_BITS = 3,      /* bits not 4 or 8 */
+    WQ_ERR_ALIGN = 4,     /* a pointer or table offset is misaligned */
+    WQ_ERR_M_RANGE = 5,   /* M outside the entry point's range (wq_gemv: 1..16) */
+    WQ_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
+    WQ_ERR_TABLE = 7      /* a tensor-table entry is inconsistent */
+};
+
+#define WQ_BLOCK 32           /* values per quantization block along K */
+#define WQ_GEMV_MAX_M 16      /* largest M accepted by wq_gemv */
+#define WQ_TABLE_ALIGN 64     /* alignment of tensors in a package and of table entries */
+
+/* Bytes of packed codes for an [N][K] tensor: N*K*bits/8. 0 on bad arguments. */
+size_t wq_q_bytes(int64_t N, int64_t K, int bits);
+/* Bytes of binary16 scales for an [N][K] tensor: N*(K/32)*2. 0 on bad arguments. */
+size_t wq_s_bytes(int64_t N, int64_t K);
+
+/*
+ * wq_pack -- quantize and pack fp32 weights w [N][K] into q and scales.
+ * Per row n and block b of 32 consecutive k (the block-32 symmetric scheme of
+ * the pages above; the scale rule and rounding are this library's reading):
+ *   amax = max |w|;  s = binary16_rne(amax / Q) with fp32 division,
+ *   Q = 7 (int4) or 127 (int8);  if s == 0 every code is 0;
+ *   else q = clamp(round_half_even(w / s), lo, hi) with fp32 division by the
+ *   stored binary16 scale, (lo, hi) = (-8, 7) or (-128, 127).
+ * Inputs must be finite with amax / Q <= 65504 (not checked here).
+ * Output is bit-exact: one correct result exists for every input.
+ */
+int wq_pack(const float *w, int64_t N, int64_t K, int bits,
+            void *q, uint16_t *scales, hipStream_t stream);
+
+/*
+ * wq_unpack -- decode packed codes q into one int8 per code, codes [N][K].
+ * Inverse of the packing layout above (test and inspection aid).
+ */
+int wq_unpack(const void *q, int64_t N, int64_t K, int bits,
+              int8_t *codes, hipStream_t stream);
+
+/*
+ * wq_gemv -- decode path (the devpost page's separate GEMV path for decode),
+ * 1 <= M <= 16. Codes are unpacked in registers and multiplied in fp32 with
+ * fused multiply-adds against the fp32 activations; each block's partial is
+ * scaled by its fp32-converted scale; lanes along K are reduced within a
+ * wavefront. Error: |y - y_exact| <= 1e-5 * sum_k |x[m,k]| |w^[n,k]|.
+ */
+int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
+            const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+
+/*
+ * wq_gemm -- prefill path (the devpost page's blocked prefill GEMM that unpacks
+ * each weight group once and reuses it across all activation rows), any M >= 1,
+ * tuned for M >= 128. Each weight tile is unpacked once into LDS as binary16
+ * (the integer codes are exact there); x is rounded to binary16 (nearest even);
+ * each 32-wide K step is one quantization block, computed by fp16 matrix-core
+ * instructions into an fp32 partial that is then scaled by that block's scale.
+ * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call.
+ */
+int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
+            const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+
+/* wq_linear -- dispatch by M: M <= 16 -> wq_gemv, M > 16 -> wq_gemm. */
+int wq_linear(const float *x, int64_t M, int64_t K, int64_t N, int bits,
+              const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+
+/*
+ * Packed package and tensor table (the devpost page, "How we built it": the
+ * packed tensors live in one container with a 64-byte-aligned tensor table).
+ * A package is one device allocation; each tensor's codes and scales start at
+ * a multiple of 64 bytes from its base. The table is an array of 64-byte
+ * descriptors; a device copy of it drives wq_gemv_grouped.
+ */
+typedef struct wq_desc {
+    int32_t bits;          /* 4 or 8 */
+    int32_t reserved;      /* must be 0 */
+    int64_t N;             /* output features (rows of q) */
+    int64_t K;             /* input features, multiple of 32 */
+    uint64_t q_off;        /* byte offset of q from the package base, multiple of 64 */
+    uint64_t s_off;        /* byte offset of scales from the package base, multiple of 64 */
+    const float *x;        /* device pointer to this call's x [M][K], 16-byte aligned */
+    float *y;              /* device pointer to this call's y [M][N], 16-byte aligned */
+    int64_t tile_begin;    /* first work tile of this tensor; set by wq_table_plan */
+} wq_desc;
+
+/*
+ * wq_table_layout -- host only. Given bits, N, K in each of `count` entries,
+ * assign q_off / s_off in table order (each at the next multiple of 64) and
+ * return the package size in *package_bytes. Other fields are left alone.
+ */
+int wq_table_layout(wq_desc *table, int count, uint64_t *package_bytes);
+
+/*
+ * wq_table_plan -- host only. For a grouped call with M rows, set tile_begin of
+ * every entry and return the total number of work tiles in *total_tiles.
+ * Validates every entry (bits, shape, 64-byte offsets, 16-byte x / y).
+ */
+int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles);
+
+/*
+ * wq_gemv_grouped -- one launch that runs the decode GEMV of every tensor in a
+ * planned table (the per-token decode step over all projections), 1 <= M <= 16.
+ * `table_dev` is a device copy of a table planned with the same M; `base` is the
+ * package base. Every call's result is bitwise equal to wq_gemv on that tensor.
+ * The calls must be independent (no call reads another call's y).
+ */
+int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
+                    int64_t total_tiles, int64_t M, hipStream_t stream);
+
+/* Human-readable text for a wq_status value (static storage). */
+const char *wq_strerror(int status);
+
+/* Library ABI version (increments on any signature or layout change). */
+int wq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol the header declares, and rejects bad arguments before any launch.
+
+Every call here fails validation on the host, so no HIP function runs.
+"""
+import ctypes
+
+import pytest
+
+import weight_only_bit_block_amd as wqa
+from weight_only_bit_block_amd import wq as W
+
+OK, NULL, SHAPE, BITS, ALIGN, MRANGE, HIP, TABLE = range(8)
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+MIS = 0x10004           # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return wqa.load()
+
+
+def test_exports_every_header_symbol(lib):
+    syms = W.header_symbols()
+    assert {"wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_grouped",
+            "wq_table_layout", "wq_table_plan", "wq_q_bytes", "wq_s_bytes", "wq_strerror",
+            "wq_abi_version"} <= set(syms)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert lib.wq_abi_version() == 1
+
+
+def test_sizes(lib):
+    assert lib.wq_q_bytes(2048, 1024, 4) == 2048 * 512
+    assert lib.wq_q_bytes(151936, 1024, 8) == 151936 * 1024
+    assert lib.wq_s_bytes(2048, 1024) == 2048 * 32 * 2
+    assert lib.wq_q_bytes(10, 33, 4) == 0 and lib.wq_q_bytes(10, 32, 5) == 0
+
+
+@pytest.mark.parametrize("fn", ["wq_gemv", "wq_gemm", "wq_linear"])
+def test_matmul_validation(lib, fn):
+    f = getattr(lib, fn)
+    # bits
+    assert f(FAKE, 1, 32, 8, 5, FAKE, FAKE, FAKE, None) == BITS
+    # shapes
+    assert f(FAKE, 1, 33, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 1, 0, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, -1, 32, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 1, 32, -8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+    # empty calls succeed without launching, even with null pointers
+    assert f(None, 0, 32, 8, 4, None, None, None, None) == OK
+    assert f(None, 3, 32, 0, 8, None, None, None, None) == OK
+    # nulls
+    assert f(None, 1, 32, 8, 4, FAKE, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 1, 32, 8, 4, None, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 1, 32, 8, 4, FAKE, None, FAKE, None) == NULL
+    assert f(FAKE, 1, 32, 8, 4, FAKE, FAKE, None, None) == NULL
+    # alignment
+    assert f(MIS, 1, 32, 8, 4, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 1, 32, 8, 4, MIS, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 1, 32, 8, 4, FAKE, MIS, FAKE, None) == ALIGN
+    assert f(FAKE, 1, 32, 8, 4, FAKE, FAKE, MIS, None) == ALIGN
+
+
+def test_gemv_m_range(lib):
+    assert lib.wq_gemv(FAKE, 17, 32, 8, 4, FAKE, FAKE, MIS, None) == ALIGN   # checks in order
+    assert lib.wq_gemv(FAKE, 17, 32, 8, 4, FAKE, FAKE, FAKE + 16, None) == MRANGE
+
+
+def test_pack_unpack_validation(lib):
+    assert lib.wq_pack(FAKE, 4, 32, 3, FAKE, FAKE, None) == BITS
+    assert lib.wq_pack(FAKE, 4, 48, 4, FAKE, FAKE, None) == SHAPE
+    assert lib.wq_pack(None, 4, 32, 4, FAKE, FAKE, None) == NULL
+    assert lib.wq_pack(FAKE, 4, 32, 4, MIS, FAKE, None) == ALIGN
+    assert lib.wq_pack(None, 0, 32, 4, None, None, None) == OK
+    assert lib.wq_unpack(FAKE, 4, 32, 4, None, None) == NULL
+    assert lib.wq_unpack(FAKE, 4, 32, 9, FAKE, None) == BITS
+
+
+def test_table_layout_and_plan(lib):
+    specs = [(4, 2048, 1024), (4, 1024, 1024), (8, 1024, 2048), (4, 3, 96), (8, 151936, 1024)]
+    arr, total = wqa.table_layout(specs)
+    end = 0
+    for i, (bits, N, K) in enumerate(specs):
+        d = arr[i]
+        assert d.q_off % 64 == 0 and d.s_off % 64 == 0
+        assert d.q_off >= end
+        assert d.s_off >= d.q_off + N * K * bits // 8
+        end = d.s_off + N * (K // 32) * 2
+    assert total % 64 == 0 and total >= end and total - end < 64
+    # plan needs x / y pointers
+    with pytest.raises(wqa.WqError):
+        wqa.table_plan(arr, 1)
+    for i in range(len(specs)):
+        arr[i].x, arr[i].y = FAKE, FAKE
+    tiles = wqa.table_plan(arr, 1)
+    begins = [arr[i].tile_begin for i in range(len(specs))]
+    assert begins[0] == 0 and begins == sorted(begins) and tiles > begins[-1]
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan(arr, 17)
+    assert e.value.status == MRANGE
+    arr[1].x = MIS
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan(arr, 1)
+    assert e.value.status == ALIGN
+    arr[1].x = FAKE
+    arr[2].q_off += 32
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan(arr, 1)
+    assert e.value.status == ALIGN
+
+
+def test_grouped_validation(lib):
+    assert lib.wq_gemv_grouped(FAKE, FAKE, 3, 10, 0, None) == MRANGE
+    assert lib.wq_gemv_grouped(FAKE, FAKE, 3, 10, 17, None) == MRANGE
+    assert lib.wq_gemv_grouped(None, FAKE, 3, 10, 1, None) == NULL
+    assert lib.wq_gemv_grouped(FAKE + 16, FAKE, 3, 10, 1, None) == ALIGN
+    assert lib.wq_gemv_grouped(FAKE, FAKE + 16, 3, 10, 1, None) == ALIGN
+    assert lib.wq_gemv_grouped(None, None, 0, 0, 1, None) == OK
+
+
+def test_strerror(lib):
+    for s in range(8):
+        assert lib.wq_strerror(s).decode()
+    assert lib.wq_strerror(99).decode() == "unknown status"

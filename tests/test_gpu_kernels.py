@@ -1,0 +1,298 @@
+"""GPU parity: pack / unpack, GEMV, GEMM and dispatch against the CPU oracle.
+
+Every expected value comes from the oracle on the same seeded inputs; the HIP
+path is called through the C ABI (via the thin Python binding).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_bit_block_amd as wqa
+from weight_only_bit_block_amd import inputs
+from tests.gpu_util import (check_gemm, check_gemv, note, scales_u16, to_dev, to_host,
+                            torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_cuda()
+    wqa.load()
+    oracle.build(force=False)
+    return t
+
+
+def _weights(N, K, seed, sigma=0.02):
+    return inputs.normal((N, K), seed=seed, sigma=sigma)
+
+
+def _crafted(N, K, bits, seed):
+    """Weights with zero blocks, exact ties, binary32 neighbours of ties,
+    binary16-subnormal scales and widely varying block magnitudes."""
+    rng = inputs.generator(seed)
+    w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    nb = K // 32
+    mags = np.float32(10.0) ** rng.uniform(-9, 2, size=(N, nb)).astype(np.float32)
+    w = (w.reshape(N, nb, 32) * mags[:, :, None]).reshape(N, K)
+    Q = 7 if bits == 4 else 127
+    for n in range(N):
+        b = int(rng.integers(0, nb))
+        w[n, 32 * b: 32 * b + 32] = 0                     # a zero block per row
+        b = int(rng.integers(0, nb))
+        s = np.float32(rng.choice([2.0 ** -7, 0.142822265625, 3.0517578125e-05, 1e-7 / 7]))
+        s = np.float32(np.float16(s))                     # an exact binary16 scale
+        blk = (rng.integers(-Q, Q, 32) + 0.5).astype(np.float32) * s
+        blk[0] = np.float32(Q) * s
+        nud = rng.integers(-1, 2, 32)
+        blk = np.where(nud > 0, np.nextafter(blk, np.float32(np.inf)), blk)
+        blk = np.where(nud < 0, np.nextafter(blk, np.float32(-np.inf)), blk)
+        blk[0] = np.float32(Q) * s
+        w[n, 32 * b: 32 * b + 32] = blk
+    return w.astype(np.float32)
+
+
+# ------------------------------------------------------------------ pack / unpack
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (257, 1024), (64, 3072)])
+def test_pack_bit_exact(torch, bits, N, K):
+    for kind, w in [("normal", _weights(N, K, (1, N, K, bits))),
+                    ("crafted", _crafted(N, K, bits, (2, N, K, bits)))]:
+        note(f"pack {kind} bits={bits} N={N} K={K}")
+        q_ref, s_ref = oracle.quantize(w, bits)
+        q, s = wqa.pack(to_dev(w), bits)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(q), q_ref), kind
+        assert np.array_equal(scales_u16(s), s_ref), kind
+        codes = wqa.unpack(q, K, bits)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(codes), oracle.decode(q_ref, K, bits)), kind
+
+
+def test_unpack_all_bytes(torch):
+    """Every byte value decodes like the oracle, incl. -8 (0x88) and -128 (0x80)."""
+    allb = np.arange(256, dtype=np.uint8)
+    q4 = np.tile(allb, 2).reshape(32, 16)
+    q8 = allb.reshape(8, 32)
+    note("unpack all bytes")
+    assert np.array_equal(to_host(wqa.unpack(to_dev(q4), 32, 4)), oracle.decode(q4, 32, 4))
+    assert np.array_equal(to_host(wqa.unpack(to_dev(q8), 32, 8)), oracle.decode(q8, 32, 8))
+
+
+# ------------------------------------------------------------------ GEMV
+GEMV_SHAPES = [(32, 1), (64, 7), (96, 33), (160, 300), (1024, 2048), (2048, 1024), (3072, 1024),
+               (4192, 129)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,N", GEMV_SHAPES)
+def test_gemv_parity(torch, bits, K, N):
+    w = _weights(N, K, (3, K, N, bits))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    for M in (1, 2, 3, 4, 5, 8, 13, 16):
+        x = inputs.normal((M, K), seed=(4, K, N, bits, M))
+        if M > 2:
+            x[1] *= 20                                    # an outlier row
+        y_ref, B = oracle.matmul(x, q_ref, s_ref, bits)
+        note(f"gemv bits={bits} M={M} K={K} N={N}")
+        y = wqa.gemv(to_dev(x), q, s, bits)
+        torch.cuda.synchronize()
+        check_gemv(to_host(y), y_ref, B, f"gemv bits={bits} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemv_one_hot_readout(torch, bits):
+    """x = e_k reads out column k of the dequantized weights bitwise, for all k."""
+    K, N = 96, 70
+    w = _crafted(N, K, bits, (5, bits))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    wh = oracle.dequant(q_ref, s_ref, K, bits)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    eye = np.eye(K, dtype=np.float32)
+    for m0 in range(0, K, 16):
+        note(f"gemv one-hot bits={bits} rows {m0}..{m0 + 15}")
+        y = to_host(wqa.gemv(to_dev(eye[m0:m0 + 16]), q, s, bits))
+        assert np.array_equal(y.astype(np.float64), wh[:, m0:m0 + 16].T)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemv_extreme_codes_zero_scales_signs(torch, bits):
+    K, N, M = 1024, 96, 4
+    nb = K // 32
+    rng = inputs.generator((6, bits))
+    q_ref = rng.integers(0, 256, (N, K * bits // 8), dtype=np.uint8)
+    q_ref[0::3] = 0x88 if bits == 4 else 0x80             # every code -8 / -128
+    s_ref = np.float16(rng.uniform(1e-3, 2e-2, (N, nb))).view(np.uint16)
+    s_ref[5] = 0                                          # zero scales, non-zero codes
+    s_ref[7, ::2] = 0
+    x = inputs.normal((M, K), seed=(7, bits))
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    y_ref, B = oracle.matmul(x, q_ref, s_ref, bits)
+    note(f"gemv extremes bits={bits}")
+    y = to_host(wqa.gemv(to_dev(x), q, s, bits))
+    check_gemv(y, y_ref, B, "extremes")
+    assert np.all(y[:, 5] == 0)
+    # sign symmetry, power-of-two homogeneity and run-to-run determinism: bitwise
+    yn = to_host(wqa.gemv(to_dev(-x), q, s, bits))
+    y8 = to_host(wqa.gemv(to_dev(x * np.float32(8.0)), q, s, bits))
+    y2 = to_host(wqa.gemv(to_dev(x), q, s, bits))
+    assert np.array_equal(yn, -y)
+    assert np.array_equal(y8, y * np.float32(8.0))
+    assert np.array_equal(y2, y)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemv_selection_matrix(torch, bits):
+    """Packed directly: one code 1 per row at k = pi(n), scale 1 -> y = x[:, pi] exactly."""
+    K, N, M = 2048, 500, 3
+    rng = inputs.generator((8, bits))
+    pi = rng.integers(0, K, N)
+    codes = np.zeros((N, K), dtype=np.int64)
+    codes[np.arange(N), pi] = 1
+    if bits == 4:
+        nib = codes & 0xF
+        q_ref = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    else:
+        q_ref = codes.astype(np.int8).view(np.uint8)
+    s_ref = np.full((N, K // 32), 0x3C00, dtype=np.uint16)   # 1.0
+    x = inputs.normal((M, K), seed=(9, bits))
+    note(f"gemv selection bits={bits}")
+    y = to_host(wqa.gemv(to_dev(x), to_dev(q_ref), to_dev(s_ref), bits))
+    assert np.array_equal(y, x[:, pi])
+
+
+# ------------------------------------------------------------------ GEMM
+GEMM_SHAPES = [(32, 5), (96, 130), (1024, 256), (3072, 384), (2048, 257)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,N", GEMM_SHAPES)
+def test_gemm_parity(torch, bits, K, N):
+    w = _weights(N, K, (10, K, N, bits))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    for M in (1, 17, 64, 128, 130, 300):
+        x = inputs.normal((M, K), seed=(11, K, N, bits, M))
+        x[M // 2] *= 20
+        y_ref, _ = oracle.matmul(x, q_ref, s_ref, bits)
+        y16, B16 = oracle.matmul(x, q_ref, s_ref, bits, x16=True)
+        note(f"gemm bits={bits} M={M} K={K} N={N}")
+        y = to_host(wqa.gemm(to_dev(x), q, s, bits))
+        check_gemm(y, y_ref, f"gemm bits={bits} M={M} K={K} N={N}")
+        # diagnostic: against the fp16-x reference the kernel is exact up to fp32 summation
+        check_gemv(y, y16, B16, f"gemm-vs-x16 bits={bits} M={M} K={K} N={N}")
+        # every row on its own (a bug confined to non-outlier rows must not hide)
+        for m in range(M):
+            den = np.linalg.norm(y_ref[m])
+            if den > 0:
+                assert np.linalg.norm(y[m] - y_ref[m]) <= 2e-3 * den, m
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_one_hot_and_selection(torch, bits):
+    K, N = 96, 150
+    w = _crafted(N, K, bits, (12, bits))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    wh = oracle.dequant(q_ref, s_ref, K, bits)
+    note(f"gemm one-hot bits={bits}")
+    y = to_host(wqa.gemm(to_dev(np.eye(K, dtype=np.float32)), to_dev(q_ref), to_dev(s_ref), bits))
+    assert np.array_equal(y.astype(np.float64), wh.T)
+    # selection with small-integer x (exact in binary16): y = x[:, pi] exactly
+    K2, N2, M2 = 1024, 300, 200
+    rng = inputs.generator((13, bits))
+    pi = rng.integers(0, K2, N2)
+    codes = np.zeros((N2, K2), dtype=np.int64)
+    codes[np.arange(N2), pi] = 1
+    if bits == 4:
+        nib = codes & 0xF
+        q2 = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    else:
+        q2 = codes.astype(np.int8).view(np.uint8)
+    s2 = np.full((N2, K2 // 32), 0x3C00, dtype=np.uint16)
+    x2 = rng.integers(-1000, 1000, (M2, K2)).astype(np.float32)
+    note(f"gemm selection bits={bits}")
+    y2 = to_host(wqa.gemm(to_dev(x2), to_dev(q2), to_dev(s2), bits))
+    assert np.array_equal(y2, x2[:, pi])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_zero_scales_and_determinism(torch, bits):
+    K, N, M = 1024, 200, 150
+    w = _weights(N, K, (14, bits))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    s_ref[3] = 0
+    x = inputs.normal((M, K), seed=(15, bits))
+    q, s, xd = to_dev(q_ref), to_dev(s_ref), to_dev(x)
+    note(f"gemm zero-scale bits={bits}")
+    y = to_host(wqa.gemm(xd, q, s, bits))
+    assert np.all(y[:, 3] == 0)
+    y2 = to_host(wqa.gemm(xd, q, s, bits))
+    assert np.array_equal(y, y2)
+    # Homogeneity and sign symmetry, on x that binary16 holds exactly (away from
+    # its subnormal range, where the rounding of 4x and x differ). Reported, and
+    # held to the elementwise bound: the matrix-core block sum need not be exactly
+    # sign-symmetric or scale-invariant in its last bit.
+    xe = x.astype(np.float16).astype(np.float32)
+    xe[np.abs(xe) < 2.0 ** -8] = 0
+    y = to_host(wqa.gemm(to_dev(xe), q, s, bits))
+    _, B16 = oracle.matmul(xe, q_ref, s_ref, bits)
+    for name, xv, f in (("sign", -xe, -1.0), ("x4", xe * np.float32(4.0), 4.0)):
+        yv = to_host(wqa.gemm(to_dev(xv), q, s, bits))
+        diff = np.abs(yv.astype(np.float64) - f * y.astype(np.float64))
+        print(f"[info] gemm {name} bits={bits}: {int(np.count_nonzero(diff))} of {diff.size} outputs "
+              f"differ, max diff/B = {float((diff / np.maximum(B16, 1e-300)).max()):.3e}", flush=True)
+        assert np.all(diff <= 1e-5 * abs(f) * B16), name
+
+
+def test_linear_dispatch(torch):
+    K, N = 1024, 300
+    w = _weights(N, K, (16,))
+    q_ref, s_ref = oracle.quantize(w, 4)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    for M in (1, 16, 17, 128):
+        x = to_dev(inputs.normal((M, K), seed=(17, M)))
+        note(f"linear M={M}")
+        y = to_host(wqa.linear(x, q, s, 4))
+        ref = to_host(wqa.gemv(x, q, s, 4) if M <= 16 else wqa.gemm(x, q, s, 4))
+        assert np.array_equal(y, ref)
+
+
+def test_empty_calls(torch):
+    q = torch.empty((0, 16), dtype=torch.uint8, device="cuda")
+    s = torch.empty((0, 1), dtype=torch.int16, device="cuda")
+    x = torch.zeros((1, 32), dtype=torch.float32, device="cuda")
+    assert wqa.gemv(x, q, s, 4).shape == (1, 0)
+    assert wqa.gemm(x, q, s, 4).shape == (1, 0)
+    x0 = torch.zeros((0, 32), dtype=torch.float32, device="cuda")
+    q1 = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    s1 = torch.zeros((4, 1), dtype=torch.int16, device="cuda")
+    assert wqa.gemv(x0, q1, s1, 4).shape == (0, 4)
+    assert wqa.gemm(x0, q1, s1, 4).shape == (0, 4)
+
+
+# ------------------------------------------------------------------ grouped decode
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 16])
+def test_grouped_matches_per_tensor(torch, M):
+    specs = [(4, 2048, 1024), (8, 1024, 1024), (4, 1024, 2048), (4, 3072, 1024), (4, 1024, 3072),
+             (8, 3000, 1024), (4, 5, 96), (8, 0, 64), (4, 77, 160)]
+    pkg = wqa.Package(specs)
+    refs = []
+    for i, (bits, N, K) in enumerate(specs):
+        w = _weights(N, K, (18, i))
+        q_ref, s_ref = oracle.quantize(w, bits)
+        pkg.q(i).copy_(to_dev(q_ref))
+        pkg.scales(i).copy_(to_dev(s_ref))
+        refs.append((q_ref, s_ref))
+    xs = [to_dev(inputs.normal((M, K), seed=(19, i, M))) for i, (_, _, K) in enumerate(specs)]
+    ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for (_, N, _) in specs]
+    call = wqa.GroupedCall(pkg, xs, ys, M)
+    note(f"grouped M={M} tiles={call.total_tiles}")
+    call()
+    torch.cuda.synchronize()
+    for i, (bits, N, K) in enumerate(specs):
+        single = to_host(wqa.gemv(xs[i], pkg.q(i), pkg.scales(i), bits))
+        got = to_host(ys[i])
+        assert np.array_equal(got, single), i
+        y_ref, B = oracle.matmul(to_host(xs[i]), refs[i][0], refs[i][1], bits)
+        check_gemv(got, y_ref, B, f"grouped tensor {i}")
