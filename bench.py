@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-only block-32 matmul on one MI355X.
+
+One step = one decode step of the Qwen3-0.6B-shaped decoder at M=1: the 197
+GEMVs (28 layers x q, k, v, o, gate, up, down in int4 block-32, plus the tied
+lm_head 1024->151936 in int8 block-32) as one grouped launch over a packed,
+64-byte-aligned tensor table. Inputs are resident in HBM before timing starts;
+three package copies (1.24 GB) are rotated so every step streams its weights
+from HBM rather than from the 256 MB last-level cache.
+
+value = packed weight bytes (codes + binary16 scales) per step / step time.
+Also reported: the roofline of the grouped GEMV kernel (algorithmic bytes per
+launch / mean launch time from HIP events on its stream), the CPU oracle timed
+on the host cores, and the prefill GEMM (M=4096 gate/up/down int4 + int8
+lm_head on the last 64 rows) in TFLOP/s against the fp16 matrix-core peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak, published
+COPIES = 3                       # rotated package copies (> 4x the 256 MB cache)
+GEMV_SOURCES = ["weight_only_bit_block_amd/csrc/wq_gemv.hip", "weight_only_bit_block_amd/csrc/wq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_grouped_decode_step_traffic.txt")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha(GEMV_SOURCES):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM leg")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a 1 GiB device copy first (counter calibration runs)")
+    return ap.parse_args()
+
+
+def build_decode(torch, wqa, wl, copies):
+    """Pack every tensor of the workload into `copies` packages; bind x / y."""
+    import numpy as np
+    specs = [(t.bits, t.N, t.K) for t in wl.tensors]
+    pkgs = [wqa.Package(specs) for _ in range(copies)]
+    host_w = {}
+    for i, t in enumerate(wl.tensors):
+        w = wl.weight(t)
+        wd = torch.from_numpy(w).cuda()
+        for p in pkgs:
+            p.pack_into(i, wd)
+        host_w[i] = w if (i < 7 or t.name == "lm_head") else None   # keep a few for the checks
+        del wd
+    xs_host = {k: wl.activation(k) for k in wl.acts}
+    xs_dev = {k: torch.from_numpy(v).cuda() for k, v in xs_host.items()}
+    xs = [xs_dev[t.act][t.act_row0: t.act_row0 + t.M] for t in wl.tensors]
+    calls, ys = [], []
+    for p in pkgs:
+        y = [torch.empty((t.M, t.N), dtype=torch.float32, device="cuda") for t in wl.tensors]
+        calls.append(wqa.GroupedCall(p, xs, y, wl.M))
+        ys.append(y)
+    torch.cuda.synchronize()
+    return pkgs, calls, ys, host_w, np
+
+
+def check_outputs(wl, ys, host_w, np, oracle):
+    """Outputs of the timed steps: identical across copies, and sampled rows of
+    the first seven projections and the lm_head equal to the oracle within the
+    GEMV bound."""
+    for r in range(1, len(ys)):
+        for a, b in zip(ys[0], ys[r]):
+            if not bool((a == b).all()):
+                raise SystemExit("bench: outputs differ between package copies")
+    rng = np.random.Generator(np.random.PCG64(12345))
+    worst = 0.0
+    for i, w in host_w.items():
+        if w is None:
+            continue
+        t = wl.tensors[i]
+        rows = np.sort(rng.choice(t.N, size=min(t.N, 256), replace=False))
+        q, s = oracle.quantize(w[rows], t.bits)
+        y_ref, B = oracle.matmul(wl.x_for(t), q, s, t.bits)
+        y = ys[0][i].cpu().numpy()[:, rows].astype(np.float64)
+        err = np.abs(y - y_ref)
+        bad = err > 1e-5 * B
+        if bad.any():
+            raise SystemExit(f"bench: parity failure in {t.name}")
+        worst = max(worst, float((err / np.maximum(1e-5 * B, 1e-300)).max()))
+    return worst
+
+
+def cpu_baseline(wl, oracle, np):
+    """The oracle on the host cores: one warmup and three timed passes over a
+    bounded sample of the decode step (the first 4 layers and the lm_head)."""
+    sample = [t for t in wl.tensors if t.layer < 4 and t.name != "lm_head"] + \
+             [t for t in wl.tensors if t.name == "lm_head"]
+    packed = []
+    wbytes = 0
+    for t in sample:
+        q, s = oracle.quantize(wl.weight(t), t.bits)
+        packed.append((t, q, s))
+        wbytes += q.nbytes + s.nbytes
+    times = []
+    for rep in range(4):
+        t0 = time.perf_counter()
+        for t, q, s in packed:
+            oracle.matmul(wl.x_for(t), q, s, t.bits)
+        dt = time.perf_counter() - t0
+        if rep > 0:
+            times.append(dt)
+    med = sorted(times)[1]
+    return {
+        "value": round(wbytes / med / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.threads_used(),
+        "kind": "oracle",
+        "sample": f"decode step M=1, layers 0-3 (28 projections) + int8 lm_head: "
+                  f"{len(sample)} GEMVs, {wbytes} packed weight bytes; median of 3 passes "
+                  f"after 1 warmup, binary64 plain loops, {med:.2f} s per pass",
+    }
+
+
+def prefill_leg(torch, wqa, inputs, steps, warmup):
+    """M=4096 gate/up/down (int4) + int8 lm_head on the last 64 rows, via wq_linear."""
+    wl = inputs.long_prefill()
+    packed = []
+    for t in wl.tensors:
+        q, s = wqa.pack(torch.from_numpy(wl.weight(t)).cuda(), t.bits)
+        packed.append((q, s))
+    xs = {k: torch.from_numpy(wl.activation(k)).cuda() for k in wl.acts}
+    outs = [torch.empty((t.M, t.N), dtype=torch.float32, device="cuda") for t in wl.tensors]
+
+    def step():
+        for i, t in enumerate(wl.tensors):
+            wqa.linear(xs[t.act][t.act_row0: t.act_row0 + t.M], packed[i][0], packed[i][1], t.bits, out=outs[i])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in wl.tensors]
+    per = [0.0] * len(wl.tensors)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for i, t in enumerate(wl.tensors):
+            ev[i][0].record(stream)
+            wqa.linear(xs[t.act][t.act_row0: t.act_row0 + t.M], packed[i][0], packed[i][1], t.bits, out=outs[i])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(len(wl.tensors)):
+            per[i] += ev[i][0].elapsed_time(ev[i][1])
+    wall = (time.perf_counter() - t0) / steps
+    per = [p / steps for p in per]                         # ms per call
+    gemm_idx = [i for i, t in enumerate(wl.tensors) if t.name != "lm_head"]
+    mlp_flops = sum(2 * wl.tensors[i].M * wl.tensors[i].N * wl.tensors[i].K for i in gemm_idx)
+    mlp_ms = sum(per[i] for i in gemm_idx)
+    lm = [i for i, t in enumerate(wl.tensors) if t.name == "lm_head"][0]
+    lt = wl.tensors[lm]
+    lm_bytes = lt.weight_bytes + 4 * lt.M * lt.K + 4 * lt.M * lt.N
+    # the down projection (K=3072, N=1024) is the dominant-shape check on the MFMA kernel
+    tflops_mlp = mlp_flops / (mlp_ms * 1e-3) / 1e12
+    return {
+        "workload": wl.name,
+        "tflops": round(wl.flops / (sum(per) * 1e-3) / 1e12, 2),
+        "ms_per_step": round(sum(per), 4),
+        "wall_ms_per_step": round(wall * 1e3, 4),
+        "mlp_gemm": {"calls": "gate, up, down at M=4096 (int4)", "tflops": round(tflops_mlp, 2),
+                     "ms": round(mlp_ms, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(tflops_mlp, 2),
+                                  "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tflops_mlp / MFMA_F16_PEAK_TFLOPS, 4)}},
+        "lm_head_m64": {"ms": round(per[lm], 4), "gbs": round(lm_bytes / (per[lm] * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(lm_bytes / (per[lm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the path runs on one GPU and multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import weight_only_bit_block_amd as wqa
+    from weight_only_bit_block_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    wqa.load()
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl = inputs.decode_step(1)
+    log(f"packing {len(wl.tensors)} tensors x {COPIES} copies ({wl.weight_bytes} B each)")
+    pkgs, calls, ys, host_w, np = build_decode(torch, wqa, wl, COPIES)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        calls[i % COPIES]()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} decode steps")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        calls[i % COPIES]()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = wl.total_bytes / (launch_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+
+    import oracle
+    worst = check_outputs(wl, ys, host_w, np, oracle)
+    log(f"timed outputs checked (worst err/bound {worst:.3f})")
+    del pkgs, calls, ys
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": "W-only int4/int8 GEMV weight GB/s (M=1) + prefill GEMM TFLOPS, % roofline",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name,
+                   "description": "one decode step at M=1: 196 int4 block-32 GEMVs (28 layers x q 1024->2048, "
+                                  "k/v 1024->1024, o 2048->1024, gate/up 1024->3072, down 3072->1024) + "
+                                  "int8 block-32 lm_head 1024->151936, one grouped launch",
+                   "weight_bytes_per_step": wl.weight_bytes,
+                   "algorithmic_bytes_per_step": wl.total_bytes,
+                   "package_copies_rotated": COPIES},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic) if traffic is not None else None),
+                     "kernel": "gemv_grouped_kernel", "launch_ms": round(launch_ms, 5),
+                     "bytes_per_launch": wl.total_bytes},
+        "parity": {"timed_outputs": "copies bitwise equal; sampled rows within 1e-5*sum|x||w|",
+                   "worst_err_over_bound": round(worst, 4)},
+    }
+    if not args.no_prefill:
+        log("prefill leg")
+        result["prefill"] = prefill_leg(torch, wqa, inputs, max(3, args.steps // 10), max(1, args.warmup // 10))
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wl, oracle, np)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
