@@ -124,7 +124,7 @@ typedef struct wq_desc {
     uint64_t s_off;        /* byte offset of scales from the package base, multiple of 64 */
     const float *x;        /* device pointer to this call's x [M][K], 16-byte aligned */
     float *y;              /* device pointer to this call's y [M][N], 16-byte aligned */
-    int64_t tile_begin;    /* first work tile of this tensor; set by wq_table_plan */
+    int64_t tile_begin;    /* first work item (workgroup) of this tensor; set by wq_table_plan */
 } wq_desc;
 
 /*
@@ -136,8 +136,10 @@ int wq_table_layout(wq_desc *table, int count, uint64_t *package_bytes);
 
 /*
  * wq_table_plan -- host only. For a grouped call with M rows, set tile_begin of
- * every entry and return the total number of work tiles in *total_tiles.
- * Validates every entry (bits, shape, 64-byte offsets, 16-byte x / y).
+ * every entry and return the total number of work items (the launch size) in
+ * *total_tiles. Validates every entry (bits, shape, 64-byte offsets, 16-byte
+ * x / y, non-overlapping codes and scales). A grouped call stages a whole x row
+ * on chip, so every entry needs K <= 4096 (WQ_ERR_SHAPE otherwise).
  */
 int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles);
 

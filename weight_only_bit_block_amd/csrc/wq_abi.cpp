@@ -47,8 +47,9 @@ inline uint64_t align64(uint64_t v) { return (v + (WQ_TABLE_ALIGN - 1)) & ~(uint
 
 int gemm_grid_ok(int64_t M, int64_t N)
 {
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    return tiles <= (int64_t)0x7FFFFFFF ? WQ_OK : WQ_ERR_SHAPE;
+    // smallest prefill tile is 64 x 256; the grid is rounded up to a multiple of 8
+    const int64_t tiles = ((M + 63) / 64) * ((N + 255) / 256);
+    return tiles <= (int64_t)0x7FFFFFF0 ? WQ_OK : WQ_ERR_SHAPE;
 }
 
 }  // namespace
@@ -112,6 +113,10 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     if (empty) return WQ_OK;
     st = gemm_grid_ok(M, N);
     if (st) return st;
+    // the prefill kernel addresses codes and activations with 32-bit offsets
+    if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= ((uint64_t)1 << 32) ||
+        (uint64_t)M * (uint64_t)K >= ((uint64_t)1 << 32) || (uint64_t)N * (uint64_t)(K / WQ_BLOCK) >= ((uint64_t)1 << 32))
+        return WQ_ERR_SHAPE;
     return hip_status(wq::launch_gemm(x, M, K, N, bits, q, scales, y, stream));
 }
 
@@ -148,7 +153,7 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
     if (count < 0) return WQ_ERR_SHAPE;
     if (!total_tiles || (count > 0 && !table)) return WQ_ERR_NULL;
     if (M < 1 || M > WQ_GEMV_MAX_M) return WQ_ERR_M_RANGE;
-    const int J = wq::gemv_grouped_j(wq::gemv_mt(M));
+    const int MT = wq::gemv_mt(M);
     int64_t cur = 0;
     for (int i = 0; i < count; ++i) {
         wq_desc &d = table[i];
@@ -165,9 +170,12 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
             if (!d.x || !d.y) return WQ_ERR_NULL;
             if (!aligned(d.x, 16) || !aligned(d.y, 16)) return WQ_ERR_ALIGN;
         }
+        if (d.K * MT * wq::kGemvChunkPad / 32 > (int64_t)MT * wq::kGemvLdsFloatsPerMT && d.N > 0)
+            return WQ_ERR_SHAPE;                // grouped launches stage a whole x row: K <= 4096
         d.tile_begin = cur;
-        const int64_t rows = wq::gemv_rows_per_tile(d.K, J);
-        cur += (d.N + rows - 1) / rows;
+        const int64_t rows = wq::gemv_rows_per_tile(d.K, wq::gemv_grouped_j(d.bits, MT));
+        const int64_t tiles = (d.N + rows - 1) / rows;
+        cur += (tiles + wq::kGroupedTilesPerWg - 1) / wq::kGroupedTilesPerWg;
         if (cur > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
     }
     *total_tiles = cur;
