@@ -1,0 +1,146 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench
+times (the grouped decode launch; wq_linear for prefill).
+
+The oracle cannot afford every output of the big workloads, so each check
+samples rows of the weights (quantization is row-local: the oracle packs the
+sampled rows of the same fp32 weights) and rows of the activations, and the
+HIP outputs at those positions must meet the acceptance rule: elementwise
+1e-5 * sum|x||w| for the GEMV, relative Frobenius 2e-3 per call (on the sampled
+rows, plus every sampled row on its own) for the GEMM. Packing is checked bit
+for bit on the sampled rows, and the grouped launch bitwise against per-tensor
+wq_gemv on every output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_bit_block_amd as wqa
+from weight_only_bit_block_amd import inputs
+from tests.gpu_util import check_gemm, check_gemv, note, scales_u16, to_dev, to_host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+ROWS_PER_TENSOR = 48
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_cuda()
+    wqa.load()
+    oracle.build(force=False)
+    return t
+
+
+def _sample(n, k, seed):
+    rng = inputs.generator(seed)
+    pick = rng.choice(n, size=min(n, k), replace=False)
+    return np.unique(np.concatenate([pick, [0, n - 1]]))
+
+
+def test_single_gemv_full(torch):
+    """Single int4 GEMV, M=1, K=1024, N=2048, seed 0: every output and byte."""
+    wl = inputs.single_gemv()
+    t = wl.tensors[0]
+    w, x = wl.weight(t), wl.x_for(t)
+    note("single gemv full")
+    q, s = wqa.pack(to_dev(w), 4)
+    y = to_host(wqa.linear(to_dev(x), q, s, 4))
+    q_ref, s_ref = oracle.quantize(w, 4)
+    assert np.array_equal(to_host(q), q_ref)
+    assert np.array_equal(scales_u16(s), s_ref)
+    y_ref, B = oracle.matmul(x, q_ref, s_ref, 4)
+    check_gemv(y, y_ref, B, "single gemv")
+
+
+def _build_package(torch, wl):
+    specs = [(t.bits, t.N, t.K) for t in wl.tensors]
+    pkg = wqa.Package(specs)
+    host = {}
+    for i, t in enumerate(wl.tensors):
+        w = wl.weight(t)
+        pkg.pack_into(i, to_dev(w))
+        rows = _sample(t.N, ROWS_PER_TENSOR, (77, i))
+        host[i] = (rows, w[rows].copy())
+    torch.cuda.synchronize()
+    return pkg, host
+
+
+@pytest.mark.parametrize("mixed,Ms", [(False, (1,)), (True, (1, 2, 4, 8, 16))])
+def test_decode_step_full(torch, mixed, Ms):
+    """The 197-GEMV decode step (int4 + int8 lm_head; or the mixed package) in one
+    grouped launch per M."""
+    wl0 = inputs.decode_step(Ms[0], mixed)
+    note(f"decode step mixed={mixed}: packing {len(wl0.tensors)} tensors")
+    pkg, host = _build_package(torch, wl0)
+    # packing bit-exact on the sampled rows of every tensor
+    for i, t in enumerate(wl0.tensors):
+        rows, w = host[i]
+        q_ref, s_ref = oracle.quantize(w, t.bits)
+        assert np.array_equal(to_host(pkg.q(i))[rows], q_ref), t.name
+        assert np.array_equal(scales_u16(pkg.scales(i))[rows], s_ref), t.name
+    for M in Ms:
+        wl = inputs.decode_step(M, mixed)
+        xs = {k: to_dev(wl.activation(k)) for k in wl.acts}
+        xl = [xs[t.act][t.act_row0: t.act_row0 + t.M] for t in wl.tensors]
+        ys = [torch.full((t.M, t.N), float("nan"), dtype=torch.float32, device="cuda") for t in wl.tensors]
+        call = wqa.GroupedCall(pkg, xl, ys, M)
+        note(f"decode step mixed={mixed} M={M}: grouped launch, {call.total_tiles} workgroups")
+        call()
+        torch.cuda.synchronize()
+        worst = 0.0
+        for i, t in enumerate(wl.tensors):
+            got = to_host(ys[i])
+            single = to_host(wqa.gemv(xl[i], pkg.q(i), pkg.scales(i), t.bits))
+            assert np.array_equal(got, single), f"{t.name}: grouped != per-tensor"
+            rows, w = host[i]
+            q_ref, s_ref = oracle.quantize(w, t.bits)
+            y_ref, B = oracle.matmul(wl.x_for(t), q_ref, s_ref, t.bits)
+            worst = max(worst, check_gemv(got[:, rows], y_ref, B, f"{t.name} M={M}"))
+        print(f"[info] decode mixed={mixed} M={M}: worst err/bound {worst:.4f}", flush=True)
+
+
+def _gemm_check(x, w, bits, y, m_rows, n_cols, what):
+    """Oracle on rows m_rows of x and columns n_cols of y."""
+    q_ref, s_ref = oracle.quantize(w[n_cols], bits)
+    y_ref, _ = oracle.matmul(x[m_rows], q_ref, s_ref, bits)
+    y16, B16 = oracle.matmul(x[m_rows], q_ref, s_ref, bits, x16=True)
+    got = y[np.ix_(m_rows, n_cols)]
+    rel = check_gemm(got, y_ref, what)
+    for r in range(len(m_rows)):
+        den = np.linalg.norm(y_ref[r])
+        if den > 0:
+            assert np.linalg.norm(got[r] - y_ref[r]) <= 2e-3 * den, f"{what} row {m_rows[r]}"
+    check_gemv(got, y16, B16, what + " vs x16")
+    return rel
+
+
+@pytest.mark.parametrize("M", [128, 1024])
+def test_prefill_layer_full(torch, M):
+    """Seven int4 projections of one layer at M=128 / 1024 with 1% outlier rows."""
+    wl = inputs.prefill_layer(M)
+    for t in wl.tensors:
+        x = wl.x_for(t)
+        w = wl.weight(t)
+        note(f"prefill M={M} {t.name}")
+        q, s = wqa.pack(to_dev(w), 4)
+        y = to_host(wqa.linear(to_dev(x), q, s, 4))
+        outl = np.where(np.abs(x).max(axis=1) > 8)[0]
+        m_rows = np.unique(np.concatenate([_sample(M, 24, (78, M, inputs.PROJ_ID[t.proj])), outl]))
+        n_cols = _sample(t.N, 512, (79, M, inputs.PROJ_ID[t.proj]))
+        rel = _gemm_check(x, w, 4, y, m_rows, n_cols, f"prefill M={M} {t.name}")
+        print(f"[info] prefill M={M} {t.name}: rel Frobenius {rel:.2e}", flush=True)
+
+
+def test_long_prefill_full(torch):
+    """M=4096 gate/up/down (int4) and the int8 lm_head on the last 64 rows."""
+    wl = inputs.long_prefill()
+    for t in wl.tensors:
+        x = wl.x_for(t)
+        w = wl.weight(t)
+        note(f"long prefill {t.name} M={t.M}")
+        q, s = wqa.pack(to_dev(w), t.bits)
+        y = to_host(wqa.linear(to_dev(x), q, s, t.bits))
+        m_rows = _sample(t.M, 16, (80, inputs.PROJ_ID[t.proj])) if t.M > 64 else np.arange(t.M)
+        n_cols = _sample(t.N, 1024, (81, inputs.PROJ_ID[t.proj]))
+        rel = _gemm_check(x, w, t.bits, y, m_rows, n_cols, f"long prefill {t.name}")
+        print(f"[info] long prefill {t.name}: rel Frobenius {rel:.2e}", flush=True)

@@ -15,9 +15,12 @@ audio tokens per second of the soniqo guide ("Limits and memory").
 
 Random recipe: numpy ``Generator(PCG64(seed))``, ``standard_normal`` drawn
 directly in float32, multiplied by the float32 standard deviation (0.02 for
-weights, 1 for activations). Every tensor after the first workload is seeded by
-``SeedSequence([config, M, layer, proj, role])`` with proj q0 k1 v2 o3 gate4
-up5 down6 lm_head7 and role 0 weight, 1 activation, 2 outlier-row choice.
+weights, 1 for activations). The single-GEMV workload draws W then x from
+PCG64(0). Every other weight tensor is seeded by ``SeedSequence([config, layer,
+proj, 0])`` (the same model at every M) and every activation by
+``SeedSequence([config, M, layer, proj, role])``, with proj q0 k1 v2 o3 gate4
+up5 down6 lm_head7 and role 1 activation, 2 outlier-row choice. Config ids:
+0 single GEMV, 1 decode step, 2 layer prefill, 3 mixed decode, 4 long prefill.
 """
 from __future__ import annotations
 
@@ -134,7 +137,7 @@ class Workload:
         if self.single_stream_seed is not None:
             w, _ = self._single_stream()
             return w
-        ss = np.random.SeedSequence([self.config, self.M, t.layer, PROJ_ID[t.proj], 0])
+        ss = np.random.SeedSequence([self.config, t.layer, PROJ_ID[t.proj], 0])
         rng = np.random.Generator(np.random.PCG64(ss))
         w = rng.standard_normal((t.N, t.K), dtype=np.float32)
         w *= np.float32(W_SIGMA)
