@@ -95,10 +95,11 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
 /*
  * wq_gemm -- prefill path (the devpost page's blocked prefill GEMM that unpacks
  * each weight group once and reuses it across all activation rows), any M >= 1,
- * tuned for M >= 128. Each weight tile is unpacked once into LDS as binary16
- * (the integer codes are exact there); x is rounded to binary16 (nearest even);
- * each 32-wide K step is one quantization block, computed by fp16 matrix-core
- * instructions into an fp32 partial that is then scaled by that block's scale.
+ * tuned for M >= 128. Packed weight tiles are staged in LDS and every code is
+ * unpacked exactly once per output tile into binary16 (the integer codes are
+ * exact there); x is rounded to binary16 (nearest even); each 32-wide K step is
+ * one quantization block, computed by fp16 matrix-core instructions into an
+ * fp32 partial that is then scaled by that block's scale.
  * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call.
  */
 int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
