@@ -49,7 +49,7 @@ struct Lds {
     static constexpr int BYTES = A_BYTES + Q_BYTES + S_BYTES;
 };
 
-template <int BITS, int BM, int KT>
+template <int BITS, int BM, int KT, int NB>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restrict__ x, int M, int K,
                                                            int N, const uint8_t *__restrict__ q,
                                                            const uint16_t *__restrict__ s,
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
     constexpr int PIECES = KT * CB / 16;        // 16-byte code pieces per row per K-tile
     constexpr int QV = BN * PIECES / kThreads;  // code pieces per thread per K-tile
     static_assert(XG >= 1 && QV >= 1 && BN * PIECES % kThreads == 0, "tile shape");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NB * L::BYTES];
 
     // XCD-aware tile order: workgroups id, id+8, id+16, ... run on one XCD; give
     // them consecutive tiles (row-major over (tm, tn)).
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
 
     const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int it = 0; it < NT; ++it) {
-        const int cur = it & 1;
+        const int cur = NB == 2 ? (it & 1) : 0;
         const int nit = it + 1 < NT ? it + 1 : it;       // the last iteration reloads itself
         issue(nit);
 
@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
             if ((MF - 1) & 1) scale_row(MF - 1, pb); else scale_row(MF - 1, pa);
         }
 
-        commit(cur ^ 1, nit);
+        if (NB == 1) lds_barrier();            // one buffer: everyone has finished reading it
+        commit(NB == 2 ? (cur ^ 1) : 0, nit);
         lds_barrier();
     }
 
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
         }
 }
 
-template <int BITS, int BM, int KT>
+template <int BITS, int BM, int KT, int NB>
 hipError_t launch_cfg(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                       const uint16_t *scales, float *y, hipStream_t stream)
 {
@@ -251,7 +252,7 @@ hipError_t launch_cfg(const float *x, int64_t M, int64_t K, int64_t N, const voi
     const int tiles_n = (int)((N + BN - 1) / BN);
     const int T = tiles_m * tiles_n;
     const unsigned grid = (unsigned)(((T + kXcds - 1) / kXcds) * kXcds);
-    gemm_kernel<BITS, BM, KT><<<grid, kThreads, 0, stream>>>(x, (int)M, (int)K, (int)N, (const uint8_t *)q,
+    gemm_kernel<BITS, BM, KT, NB><<<grid, kThreads, 0, stream>>>(x, (int)M, (int)K, (int)N, (const uint8_t *)q,
                                                              scales, y, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -261,8 +262,8 @@ hipError_t launch_cfg(const float *x, int64_t M, int64_t K, int64_t N, const voi
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
-    if (bits == 4) return launch_cfg<4, 64, 4>(x, M, K, N, q, scales, y, stream);
-    return launch_cfg<8, 64, 2>(x, M, K, N, q, scales, y, stream);
+    if (bits == 4) return launch_cfg<4, 64, 4, 2>(x, M, K, N, q, scales, y, stream);
+    return launch_cfg<8, 64, 2, 2>(x, M, K, N, q, scales, y, stream);
 }
 
 }  // namespace wq
