@@ -139,8 +139,8 @@ int wq_table_layout(wq_desc *table, int count, uint64_t *package_bytes);
  * wq_table_plan -- host only. For a grouped call with M rows, set tile_begin of
  * every entry and return the total number of work items (the launch size) in
  * *total_tiles. Validates every entry (bits, shape, 64-byte offsets, 16-byte
- * x / y, non-overlapping codes and scales). A grouped call stages a whole x row
- * on chip, so every entry needs K <= 4096 (WQ_ERR_SHAPE otherwise).
+ * x / y, non-overlapping codes and scales). Work items are dispatched in table
+ * order.
  */
 int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles);
 

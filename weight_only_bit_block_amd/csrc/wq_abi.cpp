@@ -45,6 +45,15 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HI
 
 inline uint64_t align64(uint64_t v) { return (v + (WQ_TABLE_ALIGN - 1)) & ~(uint64_t)(WQ_TABLE_ALIGN - 1); }
 
+// The decode kernels address a tensor's codes and scales with 32-bit offsets.
+inline int gemv_offsets_ok(int64_t K, int64_t N, int bits)
+{
+    const uint64_t lim = (uint64_t)1 << 32;
+    if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= lim) return WQ_ERR_SHAPE;
+    if ((uint64_t)N * (uint64_t)(K / WQ_BLOCK) * 2 >= lim) return WQ_ERR_SHAPE;
+    return WQ_OK;
+}
+
 int gemm_grid_ok(int64_t M, int64_t N)
 {
     // smallest prefill tile is 64 x 256; the grid is rounded up to a multiple of 8
@@ -101,6 +110,8 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     if (st) return st;
     if (M > WQ_GEMV_MAX_M) return WQ_ERR_M_RANGE;
     if (empty) return WQ_OK;
+    st = gemv_offsets_ok(K, N, bits);
+    if (st) return st;
     return hip_status(wq::launch_gemv(x, M, K, N, bits, q, scales, y, stream));
 }
 
@@ -153,13 +164,14 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
     if (count < 0) return WQ_ERR_SHAPE;
     if (!total_tiles || (count > 0 && !table)) return WQ_ERR_NULL;
     if (M < 1 || M > WQ_GEMV_MAX_M) return WQ_ERR_M_RANGE;
-    const int MT = wq::gemv_mt(M);
     int64_t cur = 0;
     for (int i = 0; i < count; ++i) {
         wq_desc &d = table[i];
         int st = check_bits(d.bits);
         if (st) return st;
         st = check_shape(M, d.K, d.N);
+        if (st) return st;
+        st = gemv_offsets_ok(d.K, d.N, d.bits);
         if (st) return st;
         if (d.reserved != 0) return WQ_ERR_TABLE;
         if ((d.q_off % WQ_TABLE_ALIGN) || (d.s_off % WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
@@ -170,12 +182,9 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
             if (!d.x || !d.y) return WQ_ERR_NULL;
             if (!aligned(d.x, 16) || !aligned(d.y, 16)) return WQ_ERR_ALIGN;
         }
-        if (d.K * MT * wq::kGemvChunkPad / 32 > (int64_t)MT * wq::kGemvLdsFloatsPerMT && d.N > 0)
-            return WQ_ERR_SHAPE;                // grouped launches stage a whole x row: K <= 4096
         d.tile_begin = cur;
-        const int64_t rows = wq::gemv_rows_per_tile(d.K, wq::gemv_grouped_j(d.bits, MT));
-        const int64_t tiles = (d.N + rows - 1) / rows;
-        cur += (tiles + wq::kGroupedTilesPerWg - 1) / wq::kGroupedTilesPerWg;
+        const int64_t rows = wq::gemv_geom(d.K, d.bits, d.N, true).rows;
+        cur += (d.N + rows - 1) / rows;
         if (cur > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
     }
     *total_tiles = cur;

@@ -3,26 +3,38 @@
 // The devpost page for TinyMOSS-Diarize ("How we built it") describes a
 // separate GEMV path for decode that multiplies straight out of the packed
 // weights, activations in FP32, dequantization fused, nothing materialized.
-// This is that path designed for gfx950:
+// This is that path designed for gfx950, where it is bound by the HBM stream of
+// packed codes:
 //
-//  * HBM-bound weight stream: each lane owns whole 32-value blocks of a row
-//    (16 B of int4 or 32 B of int8 codes, non-temporal 128-bit loads); G lanes
-//    share a row so a wavefront's loads are contiguous; each lane keeps J rows
-//    in flight; a workgroup walks several consecutive tiles of one tensor, and
-//    the wavefronts resident on a CU keep the memory system busy.
-//  * x is staged in LDS (padded so the 128-bit reads of 64 lanes hit distinct
-//    banks) once per workgroup when it fits, and reused across all rows.
+//  * Work items. A workgroup (4 wavefronts) computes one item: IROWS
+//    consecutive rows of one tensor for all M activation rows. G lanes of a
+//    wavefront share a row and each lane owns the 16-byte chunks li, li+G,
+//    li+2G, ... of it (one int4 block, or half an int8 block, per chunk), so
+//    the lanes of a row read G*16 contiguous bytes per load (geometry in
+//    wq_internal.h). The item's codes are loaded up front with non-temporal
+//    128-bit loads straight into registers: every byte of the item is in
+//    flight at once, and memory and arithmetic overlap across the many items
+//    resident on each compute unit (few registers per lane, so many items).
+//    Items are small (16-24 KiB of codes at the decoder's shapes), so a launch
+//    has tens of thousands of them and its tail is short.
+//  * x and the item's scales are copied into LDS by direct-to-LDS loads
+//    (global_load_lds_dwordx4: no registers), issued before the code loads; a
+//    barrier that waits only for those copies lets the code loads stay in
+//    flight across it, and the arithmetic starts on each chunk as it lands. x
+//    is stored unpadded with an XOR swizzle of its 16-byte pieces so that the
+//    128-bit reads of 16 lanes hit distinct banks.
 //  * Unpack in registers without int->float conversions (wq_decode.h); the fp32
 //    FMA takes the binary16 code directly as an operand (v_fma_mix_f32), so each
 //    product q*x is exact and is accumulated in fp32.
-//  * Per block: partial sums over the block's 32 values (two chains of 16),
-//    then acc += scale * partial in fp32; lanes of a row are reduced with a
-//    butterfly, so every lane of the group holds the same bits. The arithmetic of
-//    an output does not depend on the tile shape, so every launch shape (and
-//    the grouped launch) gives bitwise identical results.
+//  * Per chunk: two partial chains over its codes, then acc += scale * partial
+//    in fp32; lanes of a row are reduced with a DPP butterfly, so every lane of
+//    the group holds the same bits. The arithmetic of an output depends only on
+//    (K, bits): not on J, the item, M or the launch (single tensor or
+//    grouped), so every launch gives bitwise identical results.
 //
-// Error: summation depth per output is 16 + 2 + (K/32)/G + log2(G), below the
-// depth of ~160 at which fp32 rounding could reach 1e-5 * sum |x||w|.
+// Error: summation depth per output is 16 + 1 + CC/G + log2(G) (CC chunks per
+// row), far below the depth of ~160 at which fp32 rounding could reach
+// 1e-5 * sum |x||w|.
 #include "wq_internal.h"
 #include "wq_decode.h"
 
@@ -37,32 +49,102 @@ __device__ __forceinline__ float fmix(_Float16 w, float x, float acc)
     return __builtin_fmaf((float)w, x, acc);   // one v_fma_mix_f32: exact product, one rounding
 }
 
-template <int BITS, int J>
-struct RoundBuf {
-    static constexpr int NV = BITS / 4;        // 128-bit loads per block (1 for int4, 2 for int8)
-    u4 w[J][NV];
-    uint16_t s[J];
-};
-
-// Weights are streamed once: non-temporal 128-bit loads.
-template <int BITS, int J>
-__device__ __forceinline__ void load_round(RoundBuf<BITS, J> &b, const uint8_t *const (&qp)[J],
-                                           const uint16_t *const (&sp)[J], int chunk)
+// y pointers come from kernel arguments or the tensor table; both are global
+// memory, so store through the global address space.
+__device__ __forceinline__ void store_global(float *p, float v)
 {
-    constexpr int CB = BITS * 4;
+    *(__attribute__((address_space(1))) float *)p = v;
+}
+
+// Butterfly sums over aligned groups of G lanes (G a power of two <= 16, one
+// DPP row). Both lanes of every exchanged pair add the same two values, so every
+// lane of a group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int N_>
+__device__ __forceinline__ void group_sums(float (&v)[N_], int G)
+{
+    if (G >= 2) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
+        for (int i = 0; i < N_; ++i) v[i] += dpp<0xB1>(v[i]);     // quad_perm [1,0,3,2]: lane ^ 1
+    }
+    if (G >= 4) {
 #pragma unroll
-        for (int h = 0; h < RoundBuf<BITS, J>::NV; ++h)
-            b.w[j][h] = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(qp[j] + (size_t)chunk * CB) + h);
-        b.s[j] = sp[j][chunk];
+        for (int i = 0; i < N_; ++i) v[i] += dpp<0x4E>(v[i]);     // quad_perm [2,3,0,1]: lane ^ 2
+    }
+    if (G >= 8) {
+#pragma unroll
+        for (int i = 0; i < N_; ++i) v[i] += dpp<0x141>(v[i]);    // row_half_mirror: other quad of 8
+    }
+    if (G >= 16) {
+#pragma unroll
+        for (int i = 0; i < N_; ++i) v[i] += dpp<0x140>(v[i]);    // row_mirror: other 8 of 16
     }
 }
 
-// One round: every lane multiplies its block of J rows by the staged x chunk.
+// Direct-to-LDS copy of 16 bytes per active lane: lane i of the wavefront
+// writes lds_base + 16 * i (lds_base is the same for every lane).
+__device__ __forceinline__ void dma16(const void *src, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+// Copies `pieces` 16-byte pieces into LDS, spread over the 4 wavefronts: piece
+// pc (0 <= pc < pieces) is read from src(pc) and lands at dst + 16 * pc.
+template <typename F>
+__device__ __forceinline__ void copy_pieces(int pieces, uint8_t *dst, int wave, int lane, F src)
+{
+    for (int base = wave * kWave; base < pieces; base += kGemvThreads) {
+        const int pc = base + lane;
+        if (pc < pieces) dma16(src(pc), dst + (size_t)base * 16);
+    }
+}
+
+// Workgroup barrier after this wave's LDS writes and copies into LDS: waits
+// until at most N vector-memory operations of the wave are outstanding (the
+// copies were issued before the last N loads) and its LDS operations are done,
+// then s_barrier. Unlike __syncthreads() it does not wait for every global load,
+// so the last N loads stay in flight across it. The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+template <int N_>
+__device__ __forceinline__ void copies_barrier()
+{
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | (7 << 4) | ((N_ >> 4) << 14));   // vmcnt(N_) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Slot (in 16-byte pieces) of piece p (0..7) of block b in a staged x row.
+// Blocks b..b+15 read at one piece index land in 16 distinct bank groups.
+__device__ __forceinline__ int xslot(int b, int p) { return b * 8 + (p ^ ((b >> 1) & 7)); }
+
+// x rows [mg, mg+MT) over blocks [b0, b0+nb) into LDS, 16-byte pieces, swizzled.
+template <int MT>
+__device__ __forceinline__ void stage_x(const float *__restrict__ x, int M, int K, int mg, int b0, int nb,
+                                        uint8_t *xs, int wave, int lane)
+{
+    copy_pieces(MT * nb * 8, xs, wave, lane, [&](int pc) {
+        const int m = pc / (nb * 8);
+        const int rem = pc - m * nb * 8;
+        const int b = rem >> 3;
+        const int p = (rem & 7) ^ ((b >> 1) & 7);                       // piece that belongs in this slot
+        const int mm = mg + m < M ? mg + m : M - 1;
+        return reinterpret_cast<const uint8_t *>(x + (size_t)mm * K + (size_t)(b0 + b) * kBlock + p * 4);
+    });
+}
+
+// The arithmetic of one chunk index for the J rows of a lane: codes w[j] (16
+// bytes of row j) times the staged x of the chunk's block (read once for all J
+// rows), into two partial chains per (j, m); then acc += scale * (p0 + p1).
+// Piece p of the block's x row m is at xp[p] + m * xstride.
 template <int BITS, int MT, int J>
-__device__ __forceinline__ void compute_round(const RoundBuf<BITS, J> &b, const float *__restrict__ xc,
-                                              int mstride, const DecodeConsts &dc, float (&acc)[J][MT])
+__device__ __forceinline__ void chunk_fma(const u4 (&w)[J], const uint8_t *const (&xp)[8], int xstride,
+                                          const DecodeConsts &dc, const float (&sc)[J], float (&acc)[J][MT])
 {
     float p0[J][MT], p1[J][MT];
 #pragma unroll
@@ -70,201 +152,284 @@ __device__ __forceinline__ void compute_round(const RoundBuf<BITS, J> &b, const 
 #pragma unroll
         for (int m = 0; m < MT; ++m) { p0[j][m] = 0.0f; p1[j][m] = 0.0f; }
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-        float xv[MT][8];
+    for (int h = 0; h < (BITS == 4 ? 4 : 2); ++h) {       // groups of 8 codes: x pieces 2h, 2h+1 of xp
+        f4 xa[MT], xb[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const f4 a = *reinterpret_cast<const f4 *>(xc + m * mstride + sub * 8);
-            const f4 c = *reinterpret_cast<const f4 *>(xc + m * mstride + sub * 8 + 4);
-            xv[m][0] = a.x; xv[m][1] = a.y; xv[m][2] = a.z; xv[m][3] = a.w;
-            xv[m][4] = c.x; xv[m][5] = c.y; xv[m][6] = c.z; xv[m][7] = c.w;
+            xa[m] = *reinterpret_cast<const f4 *>(xp[2 * h] + m * xstride);
+            xb[m] = *reinterpret_cast<const f4 *>(xp[2 * h + 1] + m * xstride);
         }
 #pragma unroll
         for (int j = 0; j < J; ++j) {
+            h2 t0, t1, t2, t3;
             if (BITS == 4) {
-                h2 t04, t15, t26, t37;
-                decode_int4(b.w[j][0][sub], dc, t04, t15, t26, t37);
+                decode_int4(w[j][h], dc, t0, t1, t2, t3);     // (k0,k4) (k1,k5) (k2,k6) (k3,k7)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    p0[j][m] = fmix(t04.x, xv[m][0], p0[j][m]);
-                    p1[j][m] = fmix(t04.y, xv[m][4], p1[j][m]);
-                    p0[j][m] = fmix(t15.x, xv[m][1], p0[j][m]);
-                    p1[j][m] = fmix(t15.y, xv[m][5], p1[j][m]);
-                    p0[j][m] = fmix(t26.x, xv[m][2], p0[j][m]);
-                    p1[j][m] = fmix(t26.y, xv[m][6], p1[j][m]);
-                    p0[j][m] = fmix(t37.x, xv[m][3], p0[j][m]);
-                    p1[j][m] = fmix(t37.y, xv[m][7], p1[j][m]);
+                    p0[j][m] = fmix(t0.x, xa[m].x, p0[j][m]);
+                    p1[j][m] = fmix(t0.y, xb[m].x, p1[j][m]);
+                    p0[j][m] = fmix(t1.x, xa[m].y, p0[j][m]);
+                    p1[j][m] = fmix(t1.y, xb[m].y, p1[j][m]);
+                    p0[j][m] = fmix(t2.x, xa[m].z, p0[j][m]);
+                    p1[j][m] = fmix(t2.y, xb[m].z, p1[j][m]);
+                    p0[j][m] = fmix(t3.x, xa[m].w, p0[j][m]);
+                    p1[j][m] = fmix(t3.y, xb[m].w, p1[j][m]);
                 }
             } else {
-                h2 t02, t13, t46, t57;
-                decode_int8(b.w[j][sub >> 1][(sub & 1) * 2], dc, t02, t13);
-                decode_int8(b.w[j][sub >> 1][(sub & 1) * 2 + 1], dc, t46, t57);
+                decode_int8(w[j][2 * h], dc, t0, t1);         // (k0,k2) (k1,k3)
+                decode_int8(w[j][2 * h + 1], dc, t2, t3);     // (k4,k6) (k5,k7)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    p0[j][m] = fmix(t02.x, xv[m][0], p0[j][m]);
-                    p1[j][m] = fmix(t02.y, xv[m][2], p1[j][m]);
-                    p0[j][m] = fmix(t13.x, xv[m][1], p0[j][m]);
-                    p1[j][m] = fmix(t13.y, xv[m][3], p1[j][m]);
-                    p0[j][m] = fmix(t46.x, xv[m][4], p0[j][m]);
-                    p1[j][m] = fmix(t46.y, xv[m][6], p1[j][m]);
-                    p0[j][m] = fmix(t57.x, xv[m][5], p0[j][m]);
-                    p1[j][m] = fmix(t57.y, xv[m][7], p1[j][m]);
+                    p0[j][m] = fmix(t0.x, xa[m].x, p0[j][m]);
+                    p1[j][m] = fmix(t0.y, xa[m].z, p1[j][m]);
+                    p0[j][m] = fmix(t1.x, xa[m].y, p0[j][m]);
+                    p1[j][m] = fmix(t1.y, xa[m].w, p1[j][m]);
+                    p0[j][m] = fmix(t2.x, xb[m].x, p0[j][m]);
+                    p1[j][m] = fmix(t2.y, xb[m].z, p1[j][m]);
+                    p0[j][m] = fmix(t3.x, xb[m].y, p0[j][m]);
+                    p1[j][m] = fmix(t3.y, xb[m].w, p1[j][m]);
                 }
             }
         }
     }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[j][m] = __builtin_fmaf(sc[j], p0[j][m] + p1[j][m], acc[j][m]);
+}
+
+// The 8 x-piece pointers a lane reads for the chunk of block `blk` of a staged
+// segment, in the order its codes use them (int8: the chunk's half of the
+// block, pieces 4*half .. 4*half+3).
+template <int BITS>
+__device__ __forceinline__ void piece_ptrs(const uint8_t *xs, int blk, int half, const uint8_t *(&xp)[8])
+{
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int p = BITS == 4 ? k : half * 4 + (k & 3);
+        xp[k] = xs + xslot(blk, p) * 16;
+    }
+}
+
+// Reduce acc over the G lanes of each row and store rows [r0, r0 + J) for
+// activation rows [mg, mg + MT) (lane li stores the values whose index is li
+// modulo G).
+template <int MT, int J>
+__device__ __forceinline__ void reduce_store(float (&acc)[J][MT], int G, int li, int64_t r0, int64_t N, int mg,
+                                             int M, float *__restrict__ y)
+{
+    group_sums(reinterpret_cast<float (&)[J * MT]>(acc), G);
+    const int mc = (M - mg) < MT ? (M - mg) : MT;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const float sc = (float)__builtin_bit_cast(_Float16, b.s[j]);
+        const int64_t r = r0 + j;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[j][m] = __builtin_fmaf(sc, p0[j][m] + p1[j][m], acc[j][m]);
+        for (int m = 0; m < MT; ++m) {
+            const int idx = j * MT + m;
+            if ((idx & (G - 1)) == li && m < mc && r < N) store_global(y + (size_t)(mg + m) * N + r, acc[j][m]);
+        }
     }
 }
 
-// Stage x rows [mg, mg+mc) and blocks [c0, c0+nchunks) into LDS, padded rows.
-template <int MT>
-__device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, int mg, int mc, int c0,
-                                        int nchunks, float *__restrict__ xs)
+// Fast item form: G == 16 and K % 256 == 0. The row is walked in CPL/S full
+// segments of S chunks per lane; per segment the x blocks and the item's scales
+// are copied into LDS, then the J*S code loads are issued, and the barrier
+// waits for the copies only. With MLOOP the M activation rows are taken MT at a
+// time; without it, M <= MT and there is one pass.
+template <int BITS, int MT, int J, int S, bool MLOOP>
+__device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int M, int K, int64_t N,
+                                               const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
+                                               float *__restrict__ y, int64_t row0, int CPL,
+                                               uint8_t *__restrict__ lds)
 {
-    const int items = MT * nchunks * 8;        // float4 items
-    for (int i = threadIdx.x; i < items; i += kGemvThreads) {
-        const int m = i / (nchunks * 8);
-        const int rem = i - m * nchunks * 8;
-        const int c = rem >> 3;
-        const int f = rem & 7;
-        f4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (m < mc)
-            v = *reinterpret_cast<const f4 *>(x + (size_t)(mg + m) * K + (size_t)(c0 + c) * kBlock + f * 4);
-        *reinterpret_cast<f4 *>(xs + (m * nchunks + c) * kGemvChunkPad + f * 4) = v;
-    }
-}
-
-// A workgroup computes `ntiles` consecutive tiles starting at row `row0` for all
-// M activation rows. Steps are (tile, m-group, round); the weights of step s+1
-// are loaded before step s is computed.
-template <int BITS, int MT, int J>
-__device__ __forceinline__ void gemv_tiles(const float *__restrict__ x, int M, int K, int64_t N,
-                                           const uint8_t *__restrict__ q,
-                                           const uint16_t *__restrict__ s, float *__restrict__ y,
-                                           int64_t row0, int ntiles, float *__restrict__ xs,
-                                           int lds_floats)
-{
-    constexpr int CB = BITS * 4;
-    const int C = K >> 5;                      // blocks per row
-    const int G = gemv_group(K);
-    const int lg = __builtin_ctz(G);
-    const int RW = kWave >> lg;                // rows per wavefront pass
-    const int CPL = C >> lg;                   // rounds per tile
+    constexpr int G = 16, CPB = BITS / 4;
+    constexpr int RW = kWave / G;
+    constexpr int IROWS = kGemvWaves * RW * J;
+    constexpr int NB = S * G / CPB;            // blocks per segment (a multiple of 8)
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    const int slot = lane >> lg;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & (G - 1);
-    const size_t qrow = (size_t)C * CB;
-    const int64_t tile_rows = (int64_t)kGemvWaves * RW * J;
+    const int lrow0 = wave * RW * J + (lane >> 4) * J;
+    const int C = K >> 5;
+    const uint32_t qrow = (uint32_t)K * BITS / 8;     // bytes per row of codes
+    const int nseg = CPL / S;
     const DecodeConsts dc = DecodeConsts::make();
-
-    int seg = lds_floats / (MT * G * kGemvChunkPad);   // rounds staged at once
-    if (seg > CPL) seg = CPL;
-    const int n_mg = (M + MT - 1) / MT;
-    // x stays resident for the whole workgroup when one m-group and one segment cover it
-    const bool resident = (n_mg == 1) && (seg == CPL);
-    const int steps_per_tile = n_mg * CPL;
-    const int steps = ntiles * steps_per_tile;
-
-    const uint8_t *qp[J];
-    const uint16_t *sp[J];
-    auto set_rows = [&](int tile) {
-        const int64_t wrow0 = row0 + (int64_t)tile * tile_rows + (int64_t)wave * RW * J;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * qrow);   // N * qrow < 2^32 (host check)
+    uint8_t *xs = lds;                                                      // [MT][NB][8] pieces
+    uint16_t *ss = reinterpret_cast<uint16_t *>(lds + MT * NB * 128);       // [IROWS][NB]
+    uint32_t rowq[J];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            int64_t r = wrow0 + (int64_t)j * RW + slot;
-            r = r < N ? r : N - 1;             // clamp: loads stay in bounds, stores are masked
-            qp[j] = q + (size_t)r * qrow;
-            sp[j] = s + (size_t)r * C;
-        }
-    };
+    for (int j = 0; j < J; ++j) {
+        int64_t r = row0 + lrow0 + j;
+        r = r < N ? r : N - 1;                 // rows past the end reload the last row
+        rowq[j] = (uint32_t)r * qrow;
+    }
 
-    // One step of the (tile, m-group, round) sequence: issue this step's J
-    // weight loads, then compute. Loads are not carried across iterations (the
-    // compiler would otherwise wait on all of them at the loop back-edge);
-    // latency is hidden by the other wavefronts resident on the CU.
-    float acc[J][MT];
-    for (int st = 0; st < steps; ++st) {
-        const int tile = st / steps_per_tile;
-        const int rem = st - tile * steps_per_tile;
-        const int mgi = rem / CPL;
-        const int rnd = rem - mgi * CPL;
-        const int mg = mgi * MT;
-        const int mc = (M - mg) < MT ? (M - mg) : MT;
-        const int sidx = rnd / seg;            // segment of this round
-        const int c0 = sidx * seg * G;
-        const int nr = (CPL - sidx * seg) < seg ? (CPL - sidx * seg) : seg;
-        const int nchunks = nr * G;
-
-        if (rnd == 0 && mgi == 0) set_rows(tile);
-        RoundBuf<BITS, J> cur;
-        load_round<BITS, J>(cur, qp, sp, rnd * G + li);
-        if (rnd % seg == 0 && (!resident || st == 0)) {
-            lds_barrier();                     // earlier readers of xs are done
-            stage_x<MT>(x, K, mg, mc, c0, nchunks, xs);
-            lds_barrier();
-        }
-        if (rnd == 0) {
+    u4 w[J][S];
+    const int mend = MLOOP ? M : 1;            // without MLOOP, M <= MT: one pass
+    for (int mg = 0; mg < mend; mg += MT) {
+        float acc[J][MT];
 #pragma unroll
-            for (int j = 0; j < J; ++j)
+        for (int j = 0; j < J; ++j)
 #pragma unroll
-                for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
-        }
-        const float *xc = xs + ((rnd - sidx * seg) * G + li) * kGemvChunkPad;
-        compute_round<BITS, MT, J>(cur, xc, nchunks * kGemvChunkPad, dc, acc);
-
-        if (rnd == CPL - 1) {
-            // butterfly over the G lanes of a row: every lane ends with the same sum
-            for (int off = G >> 1; off > 0; off >>= 1) {
-#pragma unroll
-                for (int j = 0; j < J; ++j)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) acc[j][m] += __shfl_xor(acc[j][m], off, kWave);
+            for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
+        for (int seg = 0; seg < nseg; ++seg) {
+            const int b0 = seg * NB;
+            if (mg > 0 || seg > 0) copies_barrier<0>();                // earlier readers of LDS are done
+            const bool codes = mg == 0 || nseg > 1;
+            if (codes) {
+                // the item's scales for the segment: IROWS rows of NB binary16 values
+                copy_pieces(IROWS * NB / 8, reinterpret_cast<uint8_t *>(ss), wave, lane, [&](int pc) {
+                    const int r = pc / (NB / 8);
+                    const int k8 = pc - r * (NB / 8);
+                    int64_t row = row0 + r;
+                    row = row < N ? row : N - 1;
+                    return reinterpret_cast<const uint8_t *>(s + (size_t)row * C + b0 + k8 * 8);
+                });
             }
-            const int64_t wrow0 = row0 + (int64_t)tile * tile_rows + (int64_t)wave * RW * J;
+            stage_x<MT>(x, M, K, mg, b0, NB, xs, wave, lane);
+            if (codes) {
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int64_t r = wrow0 + (int64_t)j * RW + slot;
+                for (int c = 0; c < S; ++c)
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const int idx = j * MT + m;
-                    if ((idx & (G - 1)) == li && m < mc && r < N)
-                        y[(size_t)(mg + m) * N + r] = acc[j][m];
+                    for (int j = 0; j < J; ++j)
+                        w[j][c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             qr, rowq[j] + (uint32_t)((seg * S + c) * G + li) * 16,
+                                                             0, kNonTemporal));
+                copies_barrier<J * S>();                                 // codes stay in flight
+            } else {
+                copies_barrier<0>();
+            }
+            // Lane li reads block blk(c) = c * 16 / CPB + blk0 of the segment; the
+            // swizzle of its pieces depends on li only (int4) or on li and the parity
+            // of c (int8), so the piece pointers are set once and each chunk adds a
+            // constant: the LDS reads take immediate offsets.
+            const int blk0 = li / CPB;
+            const uint8_t *xpe[8], *xpo[8];
+            piece_ptrs<BITS>(xs, blk0, li & 1, xpe);
+            if (BITS == 8) piece_ptrs<BITS>(xs, blk0 + 8, li & 1, xpo);
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                const int blk = c * G / CPB + blk0;                      // block within the segment
+                const int cofs = (BITS == 4 ? c : (c & ~1)) * (G / CPB) * 128;
+                const uint8_t *xp[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xp[k] = ((BITS == 8 && (c & 1)) ? xpo[k] : xpe[k]) + cofs;
+                float sc[J];
+                u4 wc[J];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    sc[j] = (float)__builtin_bit_cast(_Float16, ss[(lrow0 + j) * NB + blk]);
+                    wc[j] = w[j][c];
                 }
+                chunk_fma<BITS, MT, J>(wc, xp, NB * 128, dc, sc, acc);
+                __builtin_amdgcn_sched_barrier(0);   // keep each chunk's work together (bounds live registers)
             }
         }
+        reduce_store<MT, J>(acc, G, li, row0 + lrow0, N, mg, M, y);
     }
 }
 
-template <int BITS, int MT, int J>
-__global__ __launch_bounds__(kGemvThreads, 2) void gemv_kernel(const float *__restrict__ x, int M, int K,
-                                                               int64_t N, const uint8_t *__restrict__ q,
-                                                               const uint16_t *__restrict__ s,
-                                                               float *__restrict__ y, int tiles_per_wg,
-                                                               int64_t total_tiles, int lds_floats)
+// General item form (any K % 32 == 0): one row per lane, chunk by chunk. x is
+// staged per segment of up to kGemvGenBlocks blocks; scales are read directly.
+template <int BITS, int MT, bool MLOOP>
+__device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, int M, int K, int64_t N,
+                                                  const uint8_t *__restrict__ q,
+                                                  const uint16_t *__restrict__ s, float *__restrict__ y,
+                                                  int64_t row0, const GemvGeom &g, uint8_t *__restrict__ lds)
 {
-    extern __shared__ float xs[];
-    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_wg;
-    const int64_t left = total_tiles - t0;
-    const int nt = left < tiles_per_wg ? (int)left : tiles_per_wg;
-    gemv_tiles<BITS, MT, J>(x, M, K, N, q, s, y, t0 * gemv_rows_per_tile(K, J), nt, xs, lds_floats);
+    constexpr int CPB = BITS / 4;
+    const int G = g.G;
+    const int lg = __builtin_ctz(G);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & (G - 1);
+    const int lrow = wave * (kWave >> lg) + (lane >> lg);
+    const int C = K >> 5;
+    const int CC = C * CPB;
+    const uint32_t qrow = (uint32_t)K * BITS / 8;
+    const DecodeConsts dc = DecodeConsts::make();
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * qrow);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint64_t)N * C * 2);
+    int64_t r = row0 + lrow;
+    r = r < N ? r : N - 1;
+    const uint32_t rq = (uint32_t)r * qrow, rs = (uint32_t)r * (uint32_t)C * 2;
+    const int seg_chunks = g.nb * CPB;         // chunks of a row per segment (x blocks staged at once)
+    const int mend = MLOOP ? M : 1;
+    for (int mg = 0; mg < mend; mg += MT) {
+        float acc[1][MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[0][m] = 0.0f;
+        for (int c0 = 0; c0 < CC; c0 += seg_chunks) {
+            const int b0 = c0 / CPB;
+            const int nbs = ((CC - c0) < seg_chunks ? (CC - c0) : seg_chunks) / CPB;
+            if (mg > 0 || c0 > 0) copies_barrier<0>();
+            stage_x<MT>(x, M, K, mg, b0, nbs, lds, wave, lane);
+            copies_barrier<0>();
+#pragma unroll 1
+            for (int ch = c0 + li; ch < c0 + nbs * CPB; ch += G) {
+                u4 wc[1];
+                wc[0] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(qr, rq + (uint32_t)ch * 16, 0,
+                                                                                     kNonTemporal));
+                float sc[1];
+                sc[0] = (float)__builtin_bit_cast(
+                    _Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, rs + (uint32_t)(ch / CPB) * 2, 0, 0));
+                const uint8_t *xp[8];
+                piece_ptrs<BITS>(lds, ch / CPB - b0, ch & 1, xp);
+                chunk_fma<BITS, MT, 1>(wc, xp, nbs * 128, dc, sc, acc);
+            }
+        }
+        reduce_store<MT, 1>(acc, G, li, row0 + lrow, N, mg, M, y);
+    }
 }
 
-// Grouped launch: each workgroup takes up to kGroupedTilesPerWg consecutive
-// tiles of one tensor of the table.
-template <int MT>
-__global__ __launch_bounds__(kGemvThreads, 2) void gemv_grouped_kernel(const uint8_t *__restrict__ base,
-                                                                       const wq_desc *__restrict__ table,
-                                                                       int count, int M, int lds_floats)
+template <int BITS, int MT, int J, int S, bool MLOOP>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restrict__ x, int M, int K, int64_t N,
+                                                           const uint8_t *__restrict__ q,
+                                                           const uint16_t *__restrict__ s,
+                                                           float *__restrict__ y)
 {
-    extern __shared__ float xs[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const GemvGeom g = gemv_geom(K, BITS, N, false);
+    const int64_t row0 = (int64_t)blockIdx.x * g.rows;
+    if constexpr (S == 0) gemv_item_general<BITS, MT, MLOOP>(x, M, K, N, q, s, y, row0, g, lds);
+    else gemv_item_fast<BITS, MT, J, S, MLOOP>(x, M, K, N, q, s, y, row0, g.CPL, lds);
+}
+
+// Grouped launch: workgroup b computes item b - tile_begin of the last table
+// entry whose tile_begin <= b.
+template <int BITS, int MT, bool MLOOP>
+__device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint8_t *__restrict__ q,
+                                             const uint16_t *__restrict__ s, int64_t item, uint8_t *lds)
+{
+    const int K = (int)d.K;
+    const GemvGeom g = gemv_geom(K, BITS, d.N, true);
+    const int64_t row0 = item * g.rows;
+    switch (g.kind) {
+    case kGemvJ2S2: gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
+    case kGemvJ1S2: gemv_item_fast<BITS, MT, 1, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
+    case kGemvJ1S4: gemv_item_fast<BITS, MT, 1, 4, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
+    case kGemvJ1S6:
+    case kGemvJ1S8:
+        gemv_item_fast<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+        break;
+    default: gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds); break;
+    }
+}
+
+// Wavefronts per SIMD the grouped kernel is compiled for: the kernel holds every
+// item form, and without a bound its registers follow the largest of them.
+template <int MT, bool MLOOP>
+constexpr int grouped_waves_per_simd() { return MLOOP ? 4 : MT == 1 ? 7 : MT == 2 ? 6 : 5; }
+
+template <int MT, bool MLOOP>
+__global__ __launch_bounds__(kGemvThreads, (grouped_waves_per_simd<MT, MLOOP>())) void gemv_grouped_kernel(const uint8_t *__restrict__ base,
+                                                                   const wq_desc *__restrict__ table,
+                                                                   int count, int M)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int64_t item = blockIdx.x;
-    int lo = 0, hi = count - 1;                // last entry with tile_begin <= item
+    int lo = 0, hi = count - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (table[mid].tile_begin <= item) lo = mid; else hi = mid - 1;
@@ -272,64 +437,32 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_grouped_kernel(const uin
     const wq_desc d = table[lo];
     const uint8_t *q = base + d.q_off;
     const uint16_t *s = reinterpret_cast<const uint16_t *>(base + d.s_off);
-    const int64_t t0 = (item - d.tile_begin) * kGroupedTilesPerWg;
-    if (d.bits == 4) {
-        constexpr int J = MT <= 2 ? 8 : 4;
-        const int64_t rows = gemv_rows_per_tile(d.K, J);
-        const int64_t tiles = (d.N + rows - 1) / rows;
-        const int nt = (tiles - t0) < kGroupedTilesPerWg ? (int)(tiles - t0) : kGroupedTilesPerWg;
-        gemv_tiles<4, MT, J>(d.x, M, (int)d.K, d.N, q, s, d.y, t0 * rows, nt, xs, lds_floats);
-    } else {
-        constexpr int J = MT <= 2 ? 4 : 2;
-        const int64_t rows = gemv_rows_per_tile(d.K, J);
-        const int64_t tiles = (d.N + rows - 1) / rows;
-        const int nt = (tiles - t0) < kGroupedTilesPerWg ? (int)(tiles - t0) : kGroupedTilesPerWg;
-        gemv_tiles<8, MT, J>(d.x, M, (int)d.K, d.N, q, s, d.y, t0 * rows, nt, xs, lds_floats);
-    }
+    if (d.bits == 4) grouped_item<4, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
+    else grouped_item<8, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
 }
 
-// LDS floats for staging: the whole (padded) x of an m-group if it fits the
-// budget, else as many rounds as fit (at least one).
-inline int lds_floats_for(int MT, int64_t K)
+template <int BITS, int MT, int J, int S, bool MLOOP>
+hipError_t launch_kind(const float *x, int64_t M, int64_t K, int64_t N, const void *q, const uint16_t *s,
+                       float *y, const GemvGeom &g, hipStream_t stream)
 {
-    const int G = gemv_group(K);
-    int f = MT * kGemvLdsFloatsPerMT;
-    const int64_t whole = (int64_t)MT * (K / kBlock) * kGemvChunkPad;
-    if (whole < f) f = (int)whole;
-    if (f < MT * G * kGemvChunkPad) f = MT * G * kGemvChunkPad;
-    return f;
-}
-
-template <int BITS, int MT, int J>
-hipError_t launch_j(const float *x, int64_t M, int64_t K, int64_t N, const void *q, const uint16_t *s,
-                    float *y, hipStream_t stream)
-{
-    const int64_t rows = gemv_rows_per_tile(K, J);
-    const int64_t tiles = (N + rows - 1) / rows;
-    // consecutive tiles per workgroup: keep at least ~1024 workgroups when possible
-    int tpw = (int)(tiles / 1024);
-    if (tpw < 1) tpw = 1;
-    if (tpw > 8) tpw = 8;
-    const int64_t grid = (tiles + tpw - 1) / tpw;
-    const int lds_floats = lds_floats_for(MT, K);
-    gemv_kernel<BITS, MT, J><<<(unsigned)grid, kGemvThreads, (size_t)lds_floats * sizeof(float), stream>>>(
-        x, (int)M, (int)K, N, (const uint8_t *)q, s, y, tpw, tiles, lds_floats);
+    const int64_t items = (N + g.rows - 1) / g.rows;
+    gemv_kernel<BITS, MT, J, S, MLOOP><<<(unsigned)items, kGemvThreads, gemv_lds_bytes(MT, g), stream>>>(
+        x, (int)M, (int)K, N, (const uint8_t *)q, s, y);
     return hipGetLastError();
 }
 
-template <int BITS, int MT>
+template <int BITS, int MT, bool MLOOP>
 hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                           const uint16_t *s, float *y, hipStream_t stream)
 {
-    // The grouped depth J when the launch still has >= 512 workgroups, else
-    // shallower tiles so small GEMVs spread over the chip.
-    constexpr int JG = BITS == 4 ? (MT <= 2 ? 8 : 4) : (MT <= 2 ? 4 : 2);
-    int J = JG;
-    while (J > 1 && (N + gemv_rows_per_tile(K, J) - 1) / gemv_rows_per_tile(K, J) < 512) J >>= 1;
-    switch (J) {
-    case JG: return launch_j<BITS, MT, JG>(x, M, K, N, q, s, y, stream);
-    case (JG >= 2 ? JG / 2 : 1): return launch_j<BITS, MT, (JG >= 2 ? JG / 2 : 1)>(x, M, K, N, q, s, y, stream);
-    default: return launch_j<BITS, MT, 1>(x, M, K, N, q, s, y, stream);
+    const GemvGeom g = gemv_geom(K, BITS, N, false);
+    switch (g.kind) {
+    case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
+    case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
+    case kGemvJ1S4: return launch_kind<BITS, MT, 1, 4, MLOOP>(x, M, K, N, q, s, y, g, stream);
+    case kGemvJ1S6:
+    case kGemvJ1S8: return launch_kind<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(x, M, K, N, q, s, y, g, stream);
+    default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
     }
 }
 
@@ -338,20 +471,20 @@ hipError_t launch_gemv_bits(const float *x, int64_t M, int64_t K, int64_t N, con
                             const uint16_t *s, float *y, hipStream_t stream)
 {
     switch (gemv_mt(M)) {
-    case 1: return launch_gemv_mt<BITS, 1>(x, M, K, N, q, s, y, stream);
-    case 2: return launch_gemv_mt<BITS, 2>(x, M, K, N, q, s, y, stream);
-    case 3: return launch_gemv_mt<BITS, 3>(x, M, K, N, q, s, y, stream);
-    default: return launch_gemv_mt<BITS, 4>(x, M, K, N, q, s, y, stream);
+    case 1: return launch_gemv_mt<BITS, 1, false>(x, M, K, N, q, s, y, stream);
+    case 2: return launch_gemv_mt<BITS, 2, false>(x, M, K, N, q, s, y, stream);
+    default:
+        if (M <= kGemvMaxMT) return launch_gemv_mt<BITS, 4, false>(x, M, K, N, q, s, y, stream);
+        return launch_gemv_mt<BITS, 4, true>(x, M, K, N, q, s, y, stream);
     }
 }
 
-template <int MT>
+template <int MT, bool MLOOP>
 hipError_t launch_grouped_mt(const void *base, const wq_desc *table, int count, int64_t items,
                              int64_t M, hipStream_t stream)
 {
-    const int lds_floats = MT * kGemvLdsFloatsPerMT;
-    gemv_grouped_kernel<MT><<<(unsigned)items, kGemvThreads, (size_t)lds_floats * sizeof(float), stream>>>(
-        (const uint8_t *)base, table, count, (int)M, lds_floats);
+    gemv_grouped_kernel<MT, MLOOP><<<(unsigned)items, kGemvThreads, gemv_lds_bytes_max(MT), stream>>>(
+        (const uint8_t *)base, table, count, (int)M);
     return hipGetLastError();
 }
 
@@ -368,10 +501,11 @@ hipError_t launch_gemv_grouped(const void *base, const wq_desc *table_dev, int c
                                int64_t total_items, int64_t M, hipStream_t stream)
 {
     switch (gemv_mt(M)) {
-    case 1: return launch_grouped_mt<1>(base, table_dev, count, total_items, M, stream);
-    case 2: return launch_grouped_mt<2>(base, table_dev, count, total_items, M, stream);
-    case 3: return launch_grouped_mt<3>(base, table_dev, count, total_items, M, stream);
-    default: return launch_grouped_mt<4>(base, table_dev, count, total_items, M, stream);
+    case 1: return launch_grouped_mt<1, false>(base, table_dev, count, total_items, M, stream);
+    case 2: return launch_grouped_mt<2, false>(base, table_dev, count, total_items, M, stream);
+    default:
+        if (M <= kGemvMaxMT) return launch_grouped_mt<4, false>(base, table_dev, count, total_items, M, stream);
+        return launch_grouped_mt<4, true>(base, table_dev, count, total_items, M, stream);
     }
 }
 

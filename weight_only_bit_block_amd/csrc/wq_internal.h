@@ -14,41 +14,88 @@ constexpr int kBlock = 32;          // quantization block along K
 constexpr int kWave = 64;           // gfx950 wavefront size
 
 // ---------------------------------------------------------------- GEMV geometry
-// A row of K values is C = K/32 chunks; one chunk is one quantization block
-// (16 bytes of int4 codes or 32 bytes of int8 codes). G lanes of a wavefront
-// share a row: G is the largest power of two <= 64 dividing C, so each lane
-// owns C/G chunks of the row (chunks li, li+G, li+2G, ... : one "round" each)
-// and a wavefront covers 64/G rows per pass. A tile is J passes of the four
-// wavefronts: every lane keeps J rows (J x 16 or 32 bytes) in flight.
+// A row of K codes is read in chunks of 16 bytes: one quantization block of
+// int4 codes, or half a block of int8 codes, CC = (K/32) * (bits/4) chunks per
+// row. G lanes of a wavefront share a row (G the largest power of two <= 16
+// dividing CC); lane li owns the chunks li, li+G, li+2G, ... (CPL = CC/G of
+// them), so the lanes of a row read G*16 contiguous bytes per load. A
+// workgroup item is IROWS = 4 * (64/G) * J consecutive rows of one tensor.
+//
+// Fast form (G == 16 and K % 256 == 0: every shape of the decoder): a lane owns
+// J rows and holds S of its chunks per row in registers at a time; the row is
+// walked in CPL/S segments of S chunks (S divides CPL). General form (any K %
+// 32 == 0): one row per lane, one chunk at a time.
 constexpr int kGemvThreads = 256;   // 4 wavefronts per workgroup
 constexpr int kGemvWaves = kGemvThreads / kWave;
-constexpr int kGemvMaxMT = 4;       // activation rows per pass over the weights
-constexpr int kGemvChunkPad = 36;   // floats per staged 32-float x chunk (bank spread)
-constexpr int kGemvLdsFloatsPerMT = 4608;   // x staging budget: 18 KiB per activation row
-constexpr int kGroupedTilesPerWg = 4;       // consecutive tiles of one tensor per workgroup
+constexpr int kGemvMaxMT = 4;       // activation rows per pass over the codes
+constexpr int kGemvGenBlocks = 96;  // blocks of x staged per segment in the general form
+constexpr int kNonTemporal = 2;     // cache policy of the weight loads: streamed once
 
-__host__ __device__ inline int gemv_group(int64_t K)
+enum GemvKind { kGemvJ2S2 = 0, kGemvJ1S2, kGemvJ1S4, kGemvJ1S6, kGemvJ1S8, kGemvGeneral };
+
+struct GemvGeom {
+    int G;           // lanes per row
+    int CPL;         // chunks per lane per row
+    int kind;        // GemvKind
+    int J;           // rows per lane
+    int S;           // chunks per lane per segment (fast form)
+    int64_t rows;    // rows per item (workgroup)
+    int nb;          // blocks of x (and, fast form, of scales) staged per segment
+};
+
+// Single launches with few items use one row per lane to spread over the chip;
+// the grouped launch always uses the same shape for a given (K, bits).
+__host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bool grouped)
 {
+    GemvGeom g;
+    const int cpb = bits / 4;
     const int64_t C = K / kBlock;
-    int g = 64;
-    while (C % g) g >>= 1;
+    const int64_t CC = C * cpb;
+    int G = 16;
+    while (CC % G) G >>= 1;
+    g.G = G;
+    g.CPL = (int)(CC / G);
+    g.J = 1;
+    g.S = 1;
+    g.kind = kGemvGeneral;
+    if (G == 16 && K % 256 == 0) {
+        const int64_t rows_j2 = (int64_t)kGemvWaves * 4 * 2;
+        if (g.CPL == 2) {
+            const bool few = !grouped && (N + rows_j2 - 1) / rows_j2 < 256;
+            g.kind = few ? kGemvJ1S2 : kGemvJ2S2;
+            g.J = few ? 1 : 2;
+            g.S = 2;
+        } else if (bits == 4 && g.CPL % 6 == 0) {
+            g.kind = kGemvJ1S6; g.S = 6;
+        } else if (bits == 8 && g.CPL % 8 == 0) {
+            g.kind = kGemvJ1S8; g.S = 8;
+        } else if (g.CPL % 4 == 0) {
+            g.kind = kGemvJ1S4; g.S = 4;
+        } else if (g.CPL % 2 == 0) {
+            g.kind = kGemvJ1S2; g.S = 2;
+        }
+    }
+    g.rows = (int64_t)kGemvWaves * (kWave / G) * g.J;
+    if (g.kind == kGemvGeneral) {
+        g.nb = (int)(C < kGemvGenBlocks ? C : kGemvGenBlocks);
+    } else {
+        g.nb = g.S * 16 / cpb;
+    }
     return g;
 }
 
-// Activation rows staged at once (m-group size).
-__host__ __device__ inline int gemv_mt(int64_t M) { return M < kGemvMaxMT ? (int)M : kGemvMaxMT; }
+// Activation rows staged at once (m-group size): 1, 2 or 4.
+__host__ __device__ inline int gemv_mt(int64_t M) { return M <= 2 ? (int)M : kGemvMaxMT; }
 
-// Rows in flight per lane in the grouped launch: 128 B of codes per lane for
-// MT <= 2, 64 B above (register budget).
-__host__ __device__ inline int gemv_grouped_j(int bits, int MT)
+// LDS of an item: MT staged x rows (128 bytes per block) and, in the fast form,
+// the item's scales for one segment.
+__host__ __device__ inline size_t gemv_lds_bytes(int MT, const GemvGeom &g)
 {
-    return bits == 4 ? (MT <= 2 ? 8 : 4) : (MT <= 2 ? 4 : 2);
+    const size_t sc = g.kind == kGemvGeneral ? 0 : (size_t)g.rows * g.nb * 2;
+    return (size_t)MT * g.nb * 128 + sc;
 }
-
-__host__ __device__ inline int64_t gemv_rows_per_tile(int64_t K, int J)
-{
-    return (int64_t)kGemvWaves * (kWave / gemv_group(K)) * J;
-}
+// Upper bound over every shape: nb <= 96 and rows * nb <= 32 * 96 in the fast form.
+__host__ __device__ inline size_t gemv_lds_bytes_max(int MT) { return (size_t)MT * 96 * 128 + 32 * 96 * 2; }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations,
 // then s_barrier. Unlike __syncthreads() it does not wait for outstanding global
