@@ -4,27 +4,31 @@
 // prefill GEMM that unpacks each weight group once and reuses it across all
 // activation rows. On gfx950 (wave64, fp16 matrix cores, 160 KiB LDS):
 //
-//  * A workgroup of 4 wavefronts computes a BM x 128 tile of y (BM = 128, or 64
-//    when M <= 64); wavefront w owns 32 output columns (2 fragments of 16) and
-//    all BM rows (BM/16 fragments), so each weight code of the tile is unpacked
-//    exactly once, in the registers of the wavefront that uses it, into an
-//    exact binary16 integer, and that unpack is shared by BM/16 matrix-core
-//    instructions.
+//  * A workgroup of 4 wavefronts computes a 64 x 128 tile of y; wavefront w owns
+//    32 output columns and all 64 rows (two 32 x 32 fragments), so each weight
+//    code of the tile is unpacked exactly once, in the registers of the
+//    wavefront that uses it, into an exact binary16 integer, and that unpack
+//    feeds both row fragments.
 //  * The K loop runs over stages of KT = 2 quantization blocks through two LDS
 //    buffers. The packed codes, x (fp32) and the scales of a stage are loaded
 //    into registers while the previous stage is computed, then written to the
 //    other buffer: x rounded to binary16 (nearest even) in the order the unpack
 //    produces the codes, with an XOR swizzle of its 16-byte pieces so that the
-//    128-bit fragment reads of 16 rows hit distinct banks.
-//  * Each block of 32 values is one v_mfma_f32_16x16x32_f16 per 16 x 16
+//    128-bit fragment reads of the rows hit distinct banks.
+//  * Each block of 32 values is two chained v_mfma_f32_32x32x16_f16 per 32 x 32
 //    fragment from a zero accumulator: the block's fp32 partial, which is then
 //    scaled by the block scale of its column and added to the fp32 accumulator
-//    (one fused multiply-add per output and block, taking the binary16 scale).
+//    (one fused multiply-add per output and block). The scaling of block k-1 is
+//    issued after the matrix instructions of block k, across stage boundaries,
+//    so vector and matrix work of one wavefront overlap. The 32x32x16 shape is
+//    used rather than 16x16x32 because on gfx950 it sustains twice the fp16
+//    matrix throughput per instruction issued.
 //  * Within a block the 32 values are visited in the order the unpack produces
 //    them, identically for x and the weights, so each dot product is unchanged.
 //  * Tiles are ordered so that the workgroups placed on one XCD (workgroup id
 //    modulo 8) cover consecutive tiles of a row of tiles and share x in that
-//    XCD's L2.
+//    XCD's L2. y is written with non-temporal stores: it is not read again by
+//    this kernel and would otherwise evict x from L2.
 #include "wq_internal.h"
 #include "wq_decode.h"
 
@@ -34,13 +38,14 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128;            // columns per workgroup tile (32 per wavefront)
 constexpr int KT = 2;              // quantization blocks per stage
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
-// LDS layout of one stage buffer (BM = 128 or 64 rows per workgroup tile).
+// LDS layout of one stage buffer (BM rows per workgroup tile; 64 as launched).
 //   A: x as binary16, [BM rows][KT*32 values]; row pitch 128 bytes, 16-byte
 //      slot s of row r stored at slot s ^ ((r >> 1) & 7).
 //   B: packed codes, [BN columns][KT * CB bytes].
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
 {
     using L = Stage<BITS, BM>;
     constexpr int CB = L::CB;
-    constexpr int RF = BM / 16;                     // row fragments per wavefront
+    constexpr int RF = BM / 32;                     // 32-row fragments per wavefront
     constexpr int XI = BM * KT * 4 / kThreads;      // 8-value x groups per thread per stage (4 or 2)
     constexpr int BP = BN * KT * CB / 16;           // 16-byte code pieces per stage (256 or 512)
     constexpr int QI = BP / kThreads;               // code pieces per thread per stage (1 or 2)
@@ -84,7 +89,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int fr = lane & 15, fg = lane >> 4;    // fragment row / column, k-group
     const int C = K >> 5;                        // blocks per row
     const int NT = (C + KT - 1) / KT;            // stages
     const DecodeConsts dc = DecodeConsts::make();
@@ -173,89 +177,72 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
         }
     };
 
-    f4 acc[RF][2];
+    f16v acc[RF];
 #pragma unroll
     for (int i = 0; i < RF; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
     issue(0);
     commit(0, 0);                                // waits for stage 0's loads
     __syncthreads();
     if (NT > 1) issue(1);
 
-    const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f16v zero = {};
+    const int c = wave * 32 + (lane & 31);       // this lane's column of the tile
+    const int g = lane >> 5;                     // its k-group within a K-step of 16
+    // Blocks are pipelined: the matrix work of block k is issued, then the partials
+    // of block k-1 are scaled while it runs (also across stage boundaries).
+    f16v pp[RF];                                 // partials of the previous block
+    float scp = 0.0f;                            // and its scale (0 before the first block)
+#pragma unroll
+    for (int i = 0; i < RF; ++i) pp[i] = zero;
+    auto scale_prev = [&]() {
+#pragma unroll
+        for (int i = 0; i < RF; ++i) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][v] = __builtin_fmaf(scp, pp[i][v], acc[i][v]);
+            asm volatile("" : "+v"(acc[i]));    // the scaling happens here
+        }
+    };
     for (int it = 0; it < NT; ++it) {
         const int cur = it & 1;
         const uint8_t *base = lds + cur * L::BYTES;
         const uint8_t *B = base + L::A_BYTES;
         const uint16_t *S = reinterpret_cast<const uint16_t *>(B + L::B_BYTES);
-        // Fragment reads run one step ahead of their use: the codes and scales of
-        // block kb+1 while block kb is computed, the x fragment of row i+1 while
-        // row i is computed.
-        auto read_codes = [&](int kb, uint32_t (&cw)[2][CB / 16], uint32_t &sw2) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int c = wave * 32 + j * 16 + fr;
-                const uint8_t *qp = B + c * (KT * CB) + kb * CB + fg * (CB / 4);
+        for (int kb = 0; kb < KT; ++kb) {
+            // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
+            // unpacked once and used by every row fragment
+            h8 b[2];
+            const uint8_t *qp = B + c * (KT * CB) + kb * CB;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
                 if (BITS == 4) {
-                    cw[j][0] = *reinterpret_cast<const uint32_t *>(qp);
+                    b[st] = unpack8_int4(*reinterpret_cast<const uint32_t *>(qp + (2 * st + g) * 4), dc);
                 } else {
-                    const u2 v = *reinterpret_cast<const u2 *>(qp);
-                    cw[j][0] = v.x;
-                    cw[j][CB / 16 - 1] = v.y;
+                    const u2 v = *reinterpret_cast<const u2 *>(qp + (2 * st + g) * 8);
+                    b[st] = unpack8_int8(v.x, v.y, dc);
                 }
             }
-            const uint16_t s0 = S[(wave * 32 + fr) * KT + kb], s1 = S[(wave * 32 + 16 + fr) * KT + kb];
-            sw2 = (uint32_t)s0 | ((uint32_t)s1 << 16);
-        };
-        auto read_a = [&](int kb, int i) {
-            return *reinterpret_cast<const h8 *>(base + aslot(i * 16 + fr, kb * 4 + fg) * 16);
-        };
-        uint32_t cw[2][CB / 16], sw2;
-        read_codes(0, cw, sw2);
-        h8 an = read_a(0, 0);
-        // The stage's KT*RF (block, row fragment) steps in order; step f issues the
-        // matrix work of its two fragments, then scales the partials of step f-2
-        // (two steps of matrix work in between, so the wave does not wait for them).
-        h8 b[2];
-        float sc[2], scp[2] = {0.0f, 0.0f};
-        f4 p[3][2];
+            float sc = (float)__builtin_bit_cast(_Float16, S[c * KT + kb]);
+            asm volatile("" : "+v"(sc));             // fp32 scale: plain FMAs
+            // block partial of every row fragment: two chained K-steps of 16
+            f16v p[RF];
 #pragma unroll
-        for (int f = 0; f < KT * RF + 2; ++f) {
-            const int kb = f / RF, i = f % RF;
-            if (f < KT * RF) {
-                if (i == 0) {
-                    // this lane's codes and scales of block kb, for its 2 column fragments
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        b[j] = BITS == 4 ? unpack8_int4(cw[j][0], dc) : unpack8_int8(cw[j][0], cw[j][CB / 16 - 1], dc);
-                    scp[0] = sc[0]; scp[1] = sc[1];
-                    const h2 sp = as_h2(sw2);
-                    sc[0] = (float)sp.x; sc[1] = (float)sp.y;
-                    asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));   // fp32 scales: plain FMAs below
-                    if (kb + 1 < KT) read_codes(kb + 1, cw, sw2);
-                }
-                const h8 a = an;
-                if (i + 1 < RF) an = read_a(kb, i + 1);
-                else if (kb + 1 < KT) an = read_a(kb + 1, 0);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) p[f % 3][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], zero, 0, 0, 0);
+            for (int i = 0; i < RF; ++i) {
+                const h8 a = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + g) * 16);
+                p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[0], zero, 0, 0, 0);
             }
-            if (f >= 2) {
-                const int g = f - 2, gi = g % RF;
-                // step g's block is the current one, or the previous one when a new
-                // block started within the last two steps
-                const bool cur_block = f >= KT * RF || g / RF == kb;
-                const float s0 = cur_block ? sc[0] : scp[0];
-                const float s1 = cur_block ? sc[1] : scp[1];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    acc[gi][0][v] = __builtin_fmaf(s0, p[g % 3][0][v], acc[gi][0][v]);
-                    acc[gi][1][v] = __builtin_fmaf(s1, p[g % 3][1][v], acc[gi][1][v]);
-                }
-                asm volatile("" : "+v"(acc[gi][0]), "+v"(acc[gi][1]));   // the scaling happens here
+            for (int i = 0; i < RF; ++i) {
+                const h8 a = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + 2 + g) * 16);
+                p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[1], p[i], 0, 0, 0);
             }
+            scale_prev();                            // acc += scale * partial of the previous block
+#pragma unroll
+            for (int i = 0; i < RF; ++i) pp[i] = p[i];
+            scp = sc;
         }
         if (it + 1 < NT) {
             commit(it + 1, cur ^ 1);             // waits for stage it+1's loads
@@ -263,18 +250,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
             if (it + 2 < NT) issue(it + 2);
         }
     }
+    scale_prev();
 
-    // D fragment layout: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
+    // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
+    // column l%32.
+    const int n = n0 + c;
 #pragma unroll
     for (int i = 0; i < RF; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wave * 32 + j * 16 + fr;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = m0 + i * 16 + 4 * fg + v;
-                if (m < M && n < N) y[(size_t)m * N + n] = acc[i][j][v];
-            }
+        for (int v = 0; v < 16; ++v) {
+            const int m = m0 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+            if (m < M && n < N) __builtin_nontemporal_store(acc[i][v], y + (size_t)m * N + n);
         }
 }
 
@@ -296,13 +282,8 @@ hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const vo
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
-    // 64-row tiles when M <= 64 (no matrix work on padding rows), else 128
-    if (M <= 64) {
-        if (bits == 4) return launch_bits<4, 64>(x, M, K, N, q, scales, y, stream);
-        return launch_bits<8, 64>(x, M, K, N, q, scales, y, stream);
-    }
-    if (bits == 4) return launch_bits<4, 128>(x, M, K, N, q, scales, y, stream);
-    return launch_bits<8, 128>(x, M, K, N, q, scales, y, stream);
+    if (bits == 4) return launch_bits<4, 64>(x, M, K, N, q, scales, y, stream);
+    return launch_bits<8, 64>(x, M, K, N, q, scales, y, stream);
 }
 
 }  // namespace wq
