@@ -207,6 +207,52 @@ def sequential_leg(torch, wqa, wl, pkgs, np, steps):
             "ms_per_step": round(ms, 5), "weight_gbs": round(wl.weight_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
+    """Tied-embedding lookups (wq_embed) from the packed int8 lm_head of the
+    decode package: 1 and 128 tokens (the LiteRT card's embed_1 / embed_128) and
+    4096 tokens (the long-prefill length). Each size is captured as a graph of
+    `reps` lookups and replayed; the looked-up rows are checked bitwise against
+    the oracle on the same rows."""
+    lm = [i for i, t in enumerate(wl.tensors) if t.name == "lm_head"][0]
+    t = wl.tensors[lm]
+    q, sc = pkg.q(lm), pkg.scales(lm)
+    rng = np.random.Generator(np.random.PCG64(777))
+    out = {}
+    for n in (1, 128, 4096):
+        ids_h = rng.integers(0, t.N, (reps, n)).astype(np.int32)      # a new id set per lookup
+        ids = torch.from_numpy(ids_h).cuda()
+        y = torch.empty((n, t.K), dtype=torch.float32, device="cuda")
+        wqa.embed(ids[0], q, sc, t.K, t.bits, out=y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for r in range(reps):
+                    wqa.embed(ids[r], q, sc, t.K, t.bits, out=y)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (3 * reps)
+        qr, sr = oracle.quantize(host_w[lm][ids_h[-1]], t.bits)      # y holds the last lookup
+        ref = oracle.embed(np.arange(n), qr, sr, t.K, t.bits)
+        if not np.array_equal(y.cpu().numpy().astype(np.float64), ref):
+            raise SystemExit(f"bench: embedding lookup of {n} rows differs from the oracle")
+        nbytes = n * (t.K * t.bits // 8 + t.K // 32 * 2 + 4 * t.K + 4)
+        out[f"embed_{n}"] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "bytes": nbytes}
+    out["table"] = f"int8 lm_head {t.N}x{t.K}, packed; rows bitwise equal to the oracle"
+    return out
+
+
 def prefill_leg(torch, wqa, inputs, steps, warmup):
     """M=4096 gate/up/down (int4) + int8 lm_head on the last 64 rows, via wq_linear."""
     wl = inputs.long_prefill()
@@ -329,6 +375,8 @@ def main() -> int:
     log(f"timed outputs checked (worst err/bound {worst:.3f})")
     log("sequential form (hipGraph of 197 launches)")
     seq = sequential_leg(torch, wqa, wl, pkgs, np, max(10, args.steps // 4))
+    log("tied-embedding lookups")
+    emb = embed_leg(torch, wqa, wl, pkgs[0], host_w, np, oracle)
     del pkgs, calls, ys
     torch.cuda.empty_cache()
 
@@ -361,6 +409,7 @@ def main() -> int:
         "parity": {"timed_outputs": "copies bitwise equal; sampled rows within 1e-5*sum|x||w|",
                    "worst_err_over_bound": round(worst, 4)},
         "decode_step_sequential": seq,
+        "embedding": emb,
     }
     if not args.no_prefill:
         log("prefill leg")

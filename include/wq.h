@@ -110,6 +110,21 @@ int wq_linear(const float *x, int64_t M, int64_t K, int64_t N, int bits,
               const void *q, const uint16_t *scales, float *y, hipStream_t stream);
 
 /*
+ * wq_embed -- tied token embedding (the MOSS-Transcribe-Diarize LiteRT card,
+ * "Files": the embedder file holds one tied table for the token embedding and
+ * the lm_head, with `embed_1` / `embed_128` lookups beside `logits`). The table
+ * is a packed [N][K] tensor in the layout above (normally the int8 lm_head):
+ *   out[i][k] = s[ids[i], k/32] * q[ids[i], k]   for 0 <= i < n_ids,
+ * in fp32, which is exact. ids: int32 [n_ids], 4-byte aligned; out: fp32
+ * [n_ids][K], 16-byte aligned, must not alias the table. A row whose id lies
+ * outside [0, N) is filled with quiet NaN and the table is not read for it
+ * (ids live on the device, so they are not checked on the host). n_ids == 0
+ * returns WQ_OK without launching; with N == 0, q and scales may be null.
+ */
+int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits,
+             const void *q, const uint16_t *scales, float *out, hipStream_t stream);
+
+/*
  * Packed package and tensor table (the devpost page, "How we built it": the
  * packed tensors live in one container with a 64-byte-aligned tensor table).
  * A package is one device allocation; each tensor's codes and scales start at

@@ -130,6 +130,23 @@ def dequant(q, scales, K: int, bits: int) -> np.ndarray:
     return out
 
 
+def embed(ids, q, scales, K: int, bits: int) -> np.ndarray:
+    """Tied token embedding lookup, binary64 [len(ids), K].
+
+    The MOSS-Transcribe-Diarize LiteRT card ("Files") keeps one tied table for
+    the token embedding and the lm_head (`embed_1`, `embed_128`, `logits`); a
+    lookup is the table's row for each token. The table here is the packed
+    block-32 tensor, so row ids[i] is that row of the dequantized weights.
+    Ids outside [0, N) give rows of NaN (this library's convention).
+    """
+    w = dequant(q, scales, K, bits)
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.full((ids.size, K), np.nan, dtype=np.float64)
+    ok = (ids >= 0) & (ids < w.shape[0])
+    out[ok] = w[ids[ok]]
+    return out
+
+
 def matmul(x, q, scales, bits: int, x16: bool = False, threads: int = 0):
     """y[m,n] = sum_k x[m,k] q[n,k] s[n,k/32] in binary64, with absum = sum_k |x||w^|.
 

@@ -24,10 +24,10 @@ def test_exports_every_header_symbol(lib):
     syms = W.header_symbols()
     assert {"wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_grouped",
             "wq_table_layout", "wq_table_plan", "wq_q_bytes", "wq_s_bytes", "wq_strerror",
-            "wq_abi_version"} <= set(syms)
+            "wq_embed", "wq_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.wq_abi_version() == 1
+    assert lib.wq_abi_version() == 2
 
 
 def test_sizes(lib):
@@ -75,6 +75,26 @@ def test_pack_unpack_validation(lib):
     assert lib.wq_pack(None, 0, 32, 4, None, None, None) == OK
     assert lib.wq_unpack(FAKE, 4, 32, 4, None, None) == NULL
     assert lib.wq_unpack(FAKE, 4, 32, 9, FAKE, None) == BITS
+
+
+def test_embed_validation(lib):
+    f = lib.wq_embed
+    assert f(FAKE, 4, 32, 8, 5, FAKE, FAKE, FAKE, None) == BITS
+    assert f(FAKE, 4, 48, 8, 8, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, -1, 32, 8, 8, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 4, 32, -8, 8, FAKE, FAKE, FAKE, None) == SHAPE
+    # empty lookups succeed without launching, even with null pointers
+    assert f(None, 0, 32, 8, 8, None, None, None, None) == OK
+    assert f(None, 4, 32, 8, 8, FAKE, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 4, 32, 8, 8, None, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 4, 32, 8, 8, FAKE, None, FAKE, None) == NULL
+    assert f(FAKE, 4, 32, 8, 8, FAKE, FAKE, None, None) == NULL
+    assert f(FAKE + 2, 4, 32, 8, 8, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 4, 32, 8, 8, MIS, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 4, 32, 8, 8, FAKE, MIS, FAKE, None) == ALIGN
+    assert f(FAKE, 4, 32, 8, 8, FAKE, FAKE, MIS, None) == ALIGN
+    # an empty table needs no table pointers (every row is out of range)
+    assert f(FAKE, 4, 32, 0, 8, None, None, MIS, None) == ALIGN
 
 
 def test_table_layout_and_plan(lib):

@@ -320,3 +320,41 @@ def test_threads_do_not_change_results(oracle_mod):
     y1, _ = oracle_mod.matmul(x, q, s, 4, threads=1)
     y4, _ = oracle_mod.matmul(x, q, s, 4, threads=4)
     assert np.array_equal(y1, y4)
+
+
+# ---------------------------------------------------------------- embedding lookup
+
+def test_embed_worked_examples(oracle_mod):
+    """A table built from the two worked examples: each looked-up row is the
+    example's codes times its scale (2^-7, 2^-8), exactly; a zero row stays
+    zero; the row whose only weight is 1.0 (k = 5) reads 7 * 0x3092 =
+    0.999755859375 for int4 and 127 * (2^-7 + 2^-14) = 0.99993896484375 for int8
+    (1/127 rounds to 2^-7 + 2^-14 in binary16); ids outside the table give NaN rows."""
+    w4, c4, _, _ = _read_golden("int4_block_worked_example.txt")
+    w8, c8, _, _ = _read_golden("int8_block_worked_example.txt")
+    for bits, w_mult, codes, unit, one in ((4, w4, c4, 2.0 ** -7, 0.999755859375),
+                                           (8, w8, c8, 2.0 ** -8, 0.99993896484375)):
+        w = np.zeros((3, 64), dtype=np.float32)
+        w[0, :32] = np.array(w_mult) * unit
+        w[0, 32:] = np.array(w_mult)[::-1] * unit
+        w[2, 5] = 1.0
+        q, s = oracle_mod.quantize(w, bits)
+        e = oracle_mod.embed([0, 2, 1, 0, -1, 3], q, s, 64, bits)
+        expect0 = np.concatenate([np.array(codes), np.array(codes)[::-1]]) * unit
+        assert np.array_equal(e[0], expect0) and np.array_equal(e[3], expect0)
+        assert not e[2].any()
+        assert e[1, 5] == one and np.count_nonzero(e[1]) == 1
+        assert np.isnan(e[4]).all() and np.isnan(e[5]).all()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_embed_equals_one_hot_readout(oracle_mod, bits):
+    """Looking up row n equals reading column n of the matmul with x = I
+    (the matmul is a separate routine of the oracle: y[k, n] = w^[n, k])."""
+    N, K = 37, 96
+    w = inputs.normal((N, K), seed=(40, bits)) * np.float32(0.02)
+    q, s = oracle_mod.quantize(w, bits)
+    ids = inputs.generator((41, bits)).integers(0, N, 50)
+    e = oracle_mod.embed(ids, q, s, K, bits)
+    y, _ = oracle_mod.matmul(np.eye(K, dtype=np.float32), q, s, bits)
+    assert np.array_equal(e, y.T[ids])

@@ -8,13 +8,14 @@ device memory and the current stream):
     gemv(x, q, scales, bits)            decode path, 1 <= M <= 16
     gemm(x, q, scales, bits)            prefill path (fp16 matrix cores)
     linear(x, q, scales, bits)          dispatch by M
+    embed(ids, q, scales, K, bits)      tied-embedding rows of a packed table, fp32
     Package / GroupedCall               64-byte-aligned package + one-launch decode step
 
 The library is loaded on first use and must have been built
 (``python -m weight_only_bit_block_amd.build``); there is no fallback.
 """
-from .wq import (BLOCK, GEMV_MAX_M, GroupedCall, Package, WqError, gemm, gemv, header_symbols,
-                 linear, load, pack, table_layout, table_plan, unpack)
+from .wq import (BLOCK, GEMV_MAX_M, GroupedCall, Package, WqError, embed, gemm, gemv,
+                 header_symbols, linear, load, pack, table_layout, table_plan, unpack)
 
-__all__ = ["BLOCK", "GEMV_MAX_M", "GroupedCall", "Package", "WqError", "gemm", "gemv",
+__all__ = ["BLOCK", "GEMV_MAX_M", "GroupedCall", "Package", "WqError", "embed", "gemm", "gemv",
            "header_symbols", "linear", "load", "pack", "table_layout", "table_plan", "unpack"]

@@ -56,8 +56,8 @@ inline int gemv_offsets_ok(int64_t K, int64_t N, int bits)
 
 int gemm_grid_ok(int64_t M, int64_t N)
 {
-    // smallest prefill tile is 64 x 256; the grid is rounded up to a multiple of 8
-    const int64_t tiles = ((M + 63) / 64) * ((N + 255) / 256);
+    // the prefill tile is 64 x 128; the grid is rounded up to a multiple of 8
+    const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
     return tiles <= (int64_t)0x7FFFFFF0 ? WQ_OK : WQ_ERR_SHAPE;
 }
 
@@ -129,6 +129,23 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
         (uint64_t)M * (uint64_t)K >= ((uint64_t)1 << 32) || (uint64_t)N * (uint64_t)(K / WQ_BLOCK) >= ((uint64_t)1 << 32))
         return WQ_ERR_SHAPE;
     return hip_status(wq::launch_gemm(x, M, K, N, bits, q, scales, y, stream));
+}
+
+int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits, const void *q,
+             const uint16_t *scales, float *out, hipStream_t stream)
+{
+    int st = check_bits(bits);
+    if (st) return st;
+    st = check_shape(n_ids, K, N);
+    if (st) return st;
+    if (n_ids == 0) return WQ_OK;
+    if (!ids || !out) return WQ_ERR_NULL;
+    if (N > 0 && (!q || !scales)) return WQ_ERR_NULL;
+    if (!aligned(ids, 4) || !aligned(out, 16)) return WQ_ERR_ALIGN;
+    if (N > 0 && (!aligned(q, 16) || !aligned(scales, 16))) return WQ_ERR_ALIGN;
+    // one thread per 8 outputs; the grid must fit in 32 bits
+    if ((uint64_t)n_ids * (uint64_t)(K / 8) > (uint64_t)0x7FFFFFFF * 256) return WQ_ERR_SHAPE;
+    return hip_status(wq::launch_embed(ids, n_ids, K, N, bits, q, scales, out, stream));
 }
 
 int wq_linear(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
@@ -217,6 +234,6 @@ const char *wq_strerror(int status)
     }
 }
 
-int wq_abi_version(void) { return 1; }
+int wq_abi_version(void) { return 2; }
 
 }  // extern "C"

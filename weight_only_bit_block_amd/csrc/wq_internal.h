@@ -124,6 +124,8 @@ hipError_t launch_gemv_grouped(const void *base, const wq_desc *table_dev, int c
                                int64_t total_tiles, int64_t M, hipStream_t stream);
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
                        const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+hipError_t launch_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits,
+                        const void *q, const uint16_t *scales, float *out, hipStream_t stream);
 
 }  // namespace wq
 

@@ -70,11 +70,12 @@ def load(path: Optional[str] = None):
     lib.wq_table_layout.argtypes = [P, I, ctypes.POINTER(ctypes.c_uint64)]
     lib.wq_table_plan.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64)]
     lib.wq_gemv_grouped.argtypes = [P, P, I, I64, I64, P]
+    lib.wq_embed.argtypes = [P, I64, I64, I64, I, P, P, P, P]
     lib.wq_strerror.argtypes = [I]
     lib.wq_strerror.restype = ctypes.c_char_p
     lib.wq_abi_version.argtypes = []
     for f in ("wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_table_layout",
-              "wq_table_plan", "wq_gemv_grouped", "wq_abi_version"):
+              "wq_table_plan", "wq_gemv_grouped", "wq_embed", "wq_abi_version"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -199,6 +200,28 @@ def gemm(x, q, scales, bits: int, out=None, stream=None):
 def linear(x, q, scales, bits: int, out=None, stream=None):
     """Dispatch by M: M <= 16 -> gemv, else gemm."""
     return _matmul("wq_linear", x, q, scales, bits, out, stream)
+
+
+def embed(ids, q, scales, K: int, bits: int, out=None, stream=None):
+    """Tied token embedding: out[i] = dequantized row ids[i] of the packed table
+    (q, scales) in fp32; ids outside [0, N) give rows of NaN."""
+    torch = _torch()
+    _dev_tensor(ids, torch.int32, "ids")
+    _dev_tensor(q, torch.uint8, "q")
+    _dev_tensor(scales, torch.int16, "scales")
+    _need(ids.dim() == 1, "ids must be 1-D")
+    N = q.shape[0]
+    _need(q.shape[1] == q_row_bytes(K, bits), "q has the wrong row length for K and bits")
+    _need(tuple(scales.shape) == (N, K // BLOCK), "scales must be [N, K/32]")
+    n = ids.shape[0]
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.float32, device=ids.device)
+    else:
+        _dev_tensor(out, torch.float32, "out")
+        _need(tuple(out.shape) == (n, K), "out must be [len(ids), K]")
+    _check(load().wq_embed(_ptr(ids), n, K, N, bits, _ptr(q), _ptr(scales), _ptr(out), _stream(stream)),
+           "wq_embed")
+    return out
 
 
 # ------------------------------------------------------------------ package + grouped decode
