@@ -307,6 +307,56 @@ def prefill_leg(torch, wqa, inputs, steps, warmup):
     }
 
 
+def time_grouped(torch, calls, steps, warmup):
+    """Each copy's step (one grouped launch) is captured once in a HIP graph, as a
+    decode loop would run it; the timed region replays `steps` steps back to back,
+    rotating the copies. Returns (ms per launch from HIP events on the replay
+    stream, wall-clock ms per step)."""
+    graphs = []
+    for c in calls:
+        c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                c()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
+
+
+def fused_leg(torch, wqa, inputs, np, oracle, steps, warmup):
+    """Shared-input fusion: the same decode step with q|k|v and gate|up stacked
+    along N (113 GEMVs): one grouped launch, and 113 launches in model order."""
+    wl = inputs.decode_step(1, fused=True)
+    pkgs, calls, ys, host_w, _ = build_decode(torch, wqa, wl, COPIES)
+    launch_ms, wall_ms = time_grouped(torch, calls, steps, warmup)
+    worst = check_outputs(wl, ys, host_w, np, oracle)
+    seq = sequential_leg(torch, wqa, wl, pkgs, np, max(10, steps // 4))
+    seq["form"] = f"{len(wl.tensors)} wq_gemv launches in model order, one HIP graph per package copy"
+    out = {"workload": wl.name, "gemvs": len(wl.tensors),
+           "grouped": {"ms_per_step": round(wall_ms, 5), "launch_ms": round(launch_ms, 5),
+                       "weight_gbs": round(wl.weight_bytes / (wall_ms * 1e-3) / 1e9, 1)},
+           "sequential": seq, "worst_err_over_bound": round(worst, 4)}
+    del pkgs, calls, ys
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -335,37 +385,8 @@ def main() -> int:
     log(f"packing {len(wl.tensors)} tensors x {COPIES} copies ({wl.weight_bytes} B each)")
     pkgs, calls, ys, host_w, np = build_decode(torch, wqa, wl, COPIES)
 
-    # Each copy's step (one grouped launch) is captured once in a HIP graph, as a
-    # decode loop would run it; the timed region replays K steps back to back.
-    graphs = []
-    for c in calls:
-        c()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                c()
-        torch.cuda.synchronize()
-        graphs.append(g)
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        graphs[i % COPIES].replay()
-    torch.cuda.synchronize()
-
     log(f"timing {args.steps} decode steps")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        graphs[i % COPIES].replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = ev0.elapsed_time(ev1) / args.steps     # one launch per step, back to back
-    ms_per_step = wall * 1e3 / args.steps
+    launch_ms, ms_per_step = time_grouped(torch, calls, args.steps, args.warmup)
     value = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = wl.total_bytes / (launch_ms * 1e-3) / 1e9
     traffic = read_traffic()
@@ -411,6 +432,8 @@ def main() -> int:
         "decode_step_sequential": seq,
         "embedding": emb,
     }
+    log("shared-input fusion (113 GEMVs)")
+    result["decode_step_fused"] = fused_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
     if not args.no_prefill:
         log("prefill leg")
         result["prefill"] = prefill_leg(torch, wqa, inputs, max(3, args.steps // 10), max(1, args.warmup // 10))

@@ -99,6 +99,44 @@ def test_decode_step_full(torch, mixed, Ms):
         print(f"[info] decode mixed={mixed} M={M}: worst err/bound {worst:.4f}", flush=True)
 
 
+@pytest.mark.parametrize("mixed,M", [(False, 1), (True, 4)])
+def test_decode_step_fused_full(torch, mixed, M):
+    """The fused decode step: q|k|v and gate|up stacked along N (113 GEMVs), in
+    one grouped launch and as 113 per-tensor launches. Sampled rows include the
+    first and last row of every stacked projection."""
+    wl = inputs.decode_step(M, mixed, fused=True)
+    note(f"fused decode step mixed={mixed} M={M}: packing {len(wl.tensors)} tensors")
+    specs = [(t.bits, t.N, t.K) for t in wl.tensors]
+    pkg = wqa.Package(specs)
+    host = {}
+    for i, t in enumerate(wl.tensors):
+        w = wl.weight(t)
+        pkg.pack_into(i, to_dev(w))
+        edges = np.cumsum([0] + [inputs.PROJ_N[p] for p in (t.parts or (t.proj,))]) if t.name != "lm_head" \
+            else np.array([0, t.N])
+        rows = np.unique(np.concatenate([_sample(t.N, ROWS_PER_TENSOR, (82, i)), edges[:-1], edges[1:] - 1]))
+        host[i] = (rows, w[rows].copy())
+    xs = {k: to_dev(wl.activation(k)) for k in wl.acts}
+    xl = [xs[t.act][t.act_row0: t.act_row0 + t.M] for t in wl.tensors]
+    ys = [torch.full((t.M, t.N), float("nan"), dtype=torch.float32, device="cuda") for t in wl.tensors]
+    call = wqa.GroupedCall(pkg, xl, ys, M)
+    note(f"fused decode step mixed={mixed} M={M}: grouped launch, {call.total_tiles} workgroups")
+    call()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, t in enumerate(wl.tensors):
+        got = to_host(ys[i])
+        single = to_host(wqa.gemv(xl[i], pkg.q(i), pkg.scales(i), t.bits))
+        assert np.array_equal(got, single), f"{t.name}: grouped != per-tensor"
+        rows, w = host[i]
+        q_ref, s_ref = oracle.quantize(w, t.bits)
+        assert np.array_equal(to_host(pkg.q(i))[rows], q_ref), t.name
+        assert np.array_equal(scales_u16(pkg.scales(i))[rows], s_ref), t.name
+        y_ref, B = oracle.matmul(wl.x_for(t), q_ref, s_ref, t.bits)
+        worst = max(worst, check_gemv(got[:, rows], y_ref, B, f"{t.name} M={M}"))
+    print(f"[info] fused decode mixed={mixed} M={M}: worst err/bound {worst:.4f}", flush=True)
+
+
 def _gemm_check(x, w, bits, y, m_rows, n_cols, what):
     """Oracle on rows m_rows of x and columns n_cols of y."""
     q_ref, s_ref = oracle.quantize(w[n_cols], bits)

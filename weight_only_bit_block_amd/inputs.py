@@ -54,6 +54,11 @@ LAYER_PROJS: List[Tuple[str, int, int, str]] = [
     ("up", HIDDEN, INTER, "mlp"),
     ("down", INTER, HIDDEN, "down"),
 ]
+PROJ_N = {name: N for name, _, N, _ in LAYER_PROJS}
+# Shared-input fusion: projections that read the same activation, stacked along
+# N into one tensor (q|k|v 1024->4096, gate|up 1024->6144).
+FUSED_PROJS: List[Tuple[str, Tuple[str, ...]]] = [("qkv", ("q", "k", "v")), ("o", ("o",)),
+                                                 ("gateup", ("gate", "up")), ("down", ("down",))]
 # activation group -> projection whose id seeds it
 _GROUP_SEED_PROJ = {"attn": "q", "o": "o", "mlp": "gate", "down": "down", "lm": "lm_head"}
 
@@ -69,6 +74,7 @@ class TensorSpec:
     act: str           # key of the activation it reads
     act_row0: int = 0  # first activation row it reads (for row-offset views)
     M: int = 0         # rows it reads
+    parts: Tuple[str, ...] = ()   # fused tensor: projections whose rows are stacked along N
 
     @property
     def q_bytes(self) -> int:
@@ -137,9 +143,15 @@ class Workload:
         if self.single_stream_seed is not None:
             w, _ = self._single_stream()
             return w
-        ss = np.random.SeedSequence([self.config, t.layer, PROJ_ID[t.proj], 0])
+        if t.parts:
+            # a fused tensor is its projections' own weights, stacked along N
+            return np.concatenate([self._draw(t.layer, p, PROJ_N[p], t.K) for p in t.parts], axis=0)
+        return self._draw(t.layer, t.proj, t.N, t.K)
+
+    def _draw(self, layer: int, proj: str, N: int, K: int) -> np.ndarray:
+        ss = np.random.SeedSequence([self.config, layer, PROJ_ID[proj], 0])
         rng = np.random.Generator(np.random.PCG64(ss))
-        w = rng.standard_normal((t.N, t.K), dtype=np.float32)
+        w = rng.standard_normal((N, K), dtype=np.float32)
         w *= np.float32(W_SIGMA)
         return w
 
@@ -194,27 +206,36 @@ def single_gemv() -> Workload:
                     description="one int4 GEMV, M=1, 1024->2048", single_stream_seed=0)
 
 
-def decode_step(M: int = 1, mixed: bool = False) -> Workload:
+def decode_step(M: int = 1, mixed: bool = False, fused: bool = False) -> Workload:
     """One decode step: 28 layers x 7 projections + the tied lm_head (int8).
 
     int4 everywhere but the lm_head; with ``mixed`` the attention projections
-    (q, k, v, o) are int8 and the MLP (gate, up, down) int4.
+    (q, k, v, o) are int8 and the MLP (gate, up, down) int4. With ``fused`` the
+    projections that share an input are stacked along N (q|k|v, gate|up): the
+    same weights and activations, 113 GEMVs instead of 197.
     """
     config = 3 if mixed else 1
     tensors: List[TensorSpec] = []
     acts: Dict[str, ActSpec] = {}
+    proj = {name: (K, group) for name, K, _, group in LAYER_PROJS}
     for layer in range(LAYERS):
-        for name, K, N, group in LAYER_PROJS:
+        groups = FUSED_PROJS if fused else [(name, (name,)) for name, _, _, _ in LAYER_PROJS]
+        for name, parts in groups:
+            K, group = proj[parts[0]]
+            N = sum(PROJ_N[p] for p in parts)
             bits = 8 if (mixed and group in ("attn", "o")) else 4
             key = f"L{layer}.{group}"
             if key not in acts:
                 acts[key] = _act(config, M, layer, group, K)
-            tensors.append(TensorSpec(f"L{layer}.{name}", layer, name, K, N, bits, act=key, M=M))
+            tensors.append(TensorSpec(f"L{layer}.{name}", layer, parts[0] if len(parts) == 1 else name, K, N,
+                                      bits, act=key, M=M, parts=parts if len(parts) > 1 else ()))
     acts["lm"] = _act(config, M, 0, "lm", HIDDEN)
     tensors.append(TensorSpec("lm_head", 0, "lm_head", HIDDEN, VOCAB, 8, act="lm", M=M))
     kind = "mixed int8-attn/int4-mlp" if mixed else "int4"
-    return Workload(f"decode_step_{'mixed' if mixed else 'int4'}_m{M}", config, M, tensors, acts,
-                    description=f"one decode step, M={M}, {kind}, 197 GEMVs incl. int8 lm_head")
+    return Workload(f"decode_step_{'mixed' if mixed else 'int4'}_m{M}{'_fused' if fused else ''}", config, M,
+                    tensors, acts,
+                    description=f"one decode step, M={M}, {kind}, {len(tensors)} GEMVs incl. int8 lm_head"
+                                + (", q|k|v and gate|up stacked along N" if fused else ""))
 
 
 def prefill_layer(M: int) -> Workload:
@@ -250,12 +271,14 @@ def long_prefill(M: int = 4096, lm_rows: int = 64) -> Workload:
 
 
 def workload(name: str) -> Workload:
-    """Named workloads: single_gemv, decode_step, prefill_128, prefill_1024,
-    mixed_m{1,2,4,8,16}, long_prefill."""
+    """Named workloads: single_gemv, decode_step, decode_step_fused, prefill_128,
+    prefill_1024, mixed_m{1,2,4,8,16}, long_prefill."""
     if name == "single_gemv":
         return single_gemv()
     if name == "decode_step":
         return decode_step(1, mixed=False)
+    if name == "decode_step_fused":
+        return decode_step(1, mixed=False, fused=True)
     if name.startswith("prefill_"):
         return prefill_layer(int(name.split("_")[1]))
     if name.startswith("mixed_m"):
