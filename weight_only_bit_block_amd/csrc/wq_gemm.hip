@@ -4,11 +4,15 @@
 // prefill GEMM that unpacks each weight group once and reuses it across all
 // activation rows. On gfx950 (wave64, fp16 matrix cores, 160 KiB LDS):
 //
-//  * A workgroup of 4 wavefronts computes a 64 x 128 tile of y; wavefront w owns
-//    32 output columns and all 64 rows (two 32 x 32 fragments), so each weight
-//    code of the tile is unpacked exactly once, in the registers of the
-//    wavefront that uses it, into an exact binary16 integer, and that unpack
-//    feeds both row fragments.
+//  * A group of 4 wavefronts computes a BM x 128 tile of y (BM = 64, or 32 for
+//    small problems); wavefront w owns 32 output columns and all BM rows (BM/32
+//    fragments of 32 x 32), so each weight code of the tile is unpacked exactly
+//    once, in the registers of the wavefront that uses it, into an exact
+//    binary16 integer, and that unpack feeds every row fragment.
+//  * When there are too few tiles to occupy the chip, a workgroup holds S = 2
+//    or 4 such groups that split the tile's K loop; groups 1..S-1 hand their
+//    fp32 sums to group 0 through LDS, which adds them in group order, so the
+//    result stays deterministic and no memory beyond y is written.
 //  * The K loop runs over stages of KT = 2 quantization blocks through two LDS
 //    buffers. The packed codes, x (fp32) and the scales of a stage are loaded
 //    into registers while the previous stage is computed, then written to the
@@ -61,8 +65,8 @@ struct Stage {
 
 __device__ __forceinline__ int aslot(int r, int s) { return r * (KT * 4) + (s ^ ((r >> 1) & 7)); }
 
-template <int BITS, int BM>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restrict__ x, int M, int K, int N,
+template <int BITS, int BM, int S>
+__global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1)) void gemm_kernel(const float *__restrict__ x, int M, int K, int N,
                                                            const uint8_t *__restrict__ q,
                                                            const uint16_t *__restrict__ s,
                                                            float *__restrict__ y, int tiles_m, int tiles_n)
@@ -74,7 +78,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
     constexpr int BP = BN * KT * CB / 16;           // 16-byte code pieces per stage (256 or 512)
     constexpr int QI = BP / kThreads;               // code pieces per thread per stage (1 or 2)
     static_assert(XI * kThreads == BM * KT * 4 && BP % kThreads == 0, "tile shape");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::BYTES];
+    // S groups of 4 wavefronts split the K loop; each group has its own two stage
+    // buffers, and the partial sums of groups 1..S-1 are reduced through them.
+    static_assert((S - 1) * kThreads * RF * 16 * 4 <= S * 2 * L::BYTES, "reduction fits the stage buffers");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[S * 2 * L::BYTES];
 
     // XCD-aware tile order: workgroups id, id+8, id+16, ... run on one XCD; give
     // them consecutive tiles (row-major over (tm, tn)).
@@ -86,11 +93,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
     const int tn = tile - tm * tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const int t = threadIdx.x;
+    const int t = threadIdx.x & (kThreads - 1);  // index within the K group
+    const int h = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kThreads);   // K group
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int C = K >> 5;                        // blocks per row
-    const int NT = (C + KT - 1) / KT;            // stages
+    const int NT = (C + KT - 1) / KT;            // stages of the whole K loop
+    const int NTh = (NT + S - 1) / S;            // stages of this group (past K: scale 0)
+    const int st0 = h * NTh;                     // its first stage
+    uint8_t *const lds = lds_all + h * 2 * L::BYTES;
     const DecodeConsts dc = DecodeConsts::make();
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)M * K * 4);
@@ -133,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
     u4 qv[QI];
     uint16_t sv[KT];
     auto issue = [&](int st) {
-        const int b0 = st * KT;
+        const int b0 = (st0 + st) * KT;
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
             int b = b0 + qblk[i];                // blocks past K reload the last one (scale 0)
@@ -170,10 +181,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
             *reinterpret_cast<h8 *>(base + xlds[i]) = h;
         }
         if (t < BN) {
-            uint16_t *S = reinterpret_cast<uint16_t *>(base + L::A_BYTES + L::B_BYTES);
-            const int b0 = st * KT;
+            uint16_t *Sc = reinterpret_cast<uint16_t *>(base + L::A_BYTES + L::B_BYTES);
+            const int b0 = (st0 + st) * KT;
 #pragma unroll
-            for (int k = 0; k < KT; ++k) S[t * KT + k] = b0 + k < C ? sv[k] : (uint16_t)0;
+            for (int k = 0; k < KT; ++k) Sc[t * KT + k] = b0 + k < C ? sv[k] : (uint16_t)0;
         }
     };
 
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
     issue(0);
     commit(0, 0);                                // waits for stage 0's loads
     __syncthreads();
-    if (NT > 1) issue(1);
+    if (NTh > 1) issue(1);
 
     const f16v zero = {};
     const int c = wave * 32 + (lane & 31);       // this lane's column of the tile
@@ -205,11 +216,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
             asm volatile("" : "+v"(acc[i]));    // the scaling happens here
         }
     };
-    for (int it = 0; it < NT; ++it) {
+    for (int it = 0; it < NTh; ++it) {
         const int cur = it & 1;
         const uint8_t *base = lds + cur * L::BYTES;
         const uint8_t *B = base + L::A_BYTES;
-        const uint16_t *S = reinterpret_cast<const uint16_t *>(B + L::B_BYTES);
+        const uint16_t *Sc = reinterpret_cast<const uint16_t *>(B + L::B_BYTES);
 #pragma unroll
         for (int kb = 0; kb < KT; ++kb) {
             // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
                     b[st] = unpack8_int8(v.x, v.y, dc);
                 }
             }
-            float sc = (float)__builtin_bit_cast(_Float16, S[c * KT + kb]);
+            float sc = (float)__builtin_bit_cast(_Float16, Sc[c * KT + kb]);
             asm volatile("" : "+v"(sc));             // fp32 scale: plain FMAs
             // block partial of every row fragment: two chained K-steps of 16
             f16v p[RF];
@@ -244,13 +255,34 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
             for (int i = 0; i < RF; ++i) pp[i] = p[i];
             scp = sc;
         }
-        if (it + 1 < NT) {
+        if (it + 1 < NTh) {
             commit(it + 1, cur ^ 1);             // waits for stage it+1's loads
             __syncthreads();                     // every wave is done with buffer cur
-            if (it + 2 < NT) issue(it + 2);
+            if (it + 2 < NTh) issue(it + 2);
         }
     }
     scale_prev();
+
+    if constexpr (S > 1) {
+        // groups 1..S-1 hand their partial sums to group 0 through LDS, which
+        // adds them in group order (a fixed order: results are deterministic)
+        float *red = reinterpret_cast<float *>(lds_all);
+        __syncthreads();                         // every group is done with its buffers
+        if (h > 0) {
+#pragma unroll
+            for (int i = 0; i < RF; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) red[(((h - 1) * RF + i) * 16 + v) * kThreads + t] = acc[i][v];
+        }
+        __syncthreads();
+        if (h > 0) return;
+#pragma unroll
+        for (int j = 1; j < S; ++j)
+#pragma unroll
+            for (int i = 0; i < RF; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][v] += red[(((j - 1) * RF + i) * 16 + v) * kThreads + t];
+    }
 
     // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
     // column l%32.
@@ -264,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const float *__restri
         }
 }
 
-template <int BITS, int BM>
+template <int BITS, int BM, int S>
 hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
@@ -272,9 +304,25 @@ hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const vo
     const int tiles_n = (int)((N + BN - 1) / BN);
     const int T = tiles_m * tiles_n;
     const unsigned grid = (unsigned)(((T + kXcds - 1) / kXcds) * kXcds);
-    gemm_kernel<BITS, BM><<<grid, kThreads, 0, stream>>>(x, (int)M, (int)K, (int)N, (const uint8_t *)q, scales,
-                                                         y, tiles_m, tiles_n);
+    gemm_kernel<BITS, BM, S><<<grid, kThreads * S, 0, stream>>>(x, (int)M, (int)K, (int)N, (const uint8_t *)q,
+                                                                scales, y, tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+// Tile height and K split. With at least 256 tiles of 64 x 128 (one or more
+// per CU), one group of 4 wavefronts per tile. Fewer: 32-row tiles with the K
+// loop of each tile split over 4 groups (2 when it has fewer than 4 stages), so
+// every SIMD runs several wavefronts; the time of a tile is then about a quarter
+// of its serial K loop.
+template <int BITS>
+hipError_t launch_shape(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
+                        const uint16_t *scales, float *y, hipStream_t stream)
+{
+    const int64_t tn = (N + BN - 1) / BN;
+    const int64_t stages = (K / 32 + KT - 1) / KT;
+    if (((M + 63) / 64) * tn >= 256 || stages < 2) return launch_bits<BITS, 64, 1>(x, M, K, N, q, scales, y, stream);
+    if (stages < 4) return launch_bits<BITS, 32, 2>(x, M, K, N, q, scales, y, stream);
+    return launch_bits<BITS, 32, 4>(x, M, K, N, q, scales, y, stream);
 }
 
 }  // namespace
@@ -282,8 +330,8 @@ hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const vo
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
-    if (bits == 4) return launch_bits<4, 64>(x, M, K, N, q, scales, y, stream);
-    return launch_bits<8, 64>(x, M, K, N, q, scales, y, stream);
+    if (bits == 4) return launch_shape<4>(x, M, K, N, q, scales, y, stream);
+    return launch_shape<8>(x, M, K, N, q, scales, y, stream);
 }
 
 }  // namespace wq
