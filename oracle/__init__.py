@@ -70,8 +70,8 @@ def _ptr(a: np.ndarray) -> int:
 
 
 def _check_bits(bits: int) -> None:
-    if bits not in (4, 8):
-        raise ValueError("bits must be 4 or 8")
+    if bits not in (4, 5, 8):
+        raise ValueError("bits must be 4, 5 or 8")
 
 
 def q_row_bytes(K: int, bits: int) -> int:
@@ -108,7 +108,8 @@ def quantize(w, bits: int):
 
 
 def decode(q, K: int, bits: int) -> np.ndarray:
-    """Packed bytes [N, K*bits/8] -> int8 codes [N, K]."""
+    """Packed bytes [N, K*bits/8] -> int8 codes [N, K] (int5: a row is the K/2
+    bytes of low nibbles, then the K/8 bytes of bit 4)."""
     _check_bits(bits)
     q = np.ascontiguousarray(q, dtype=np.uint8)
     N = q.shape[0]

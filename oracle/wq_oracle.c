@@ -24,6 +24,13 @@
  *            a block whose stored scale is zero gets all-zero codes;
  *   - int4 layout: two nibbles per byte, low nibble = even k, two's complement;
  *     int8 layout: one two's-complement byte per code; rows of length K.
+ *   - int5 (the soniqo MOSS guide, "Use" and "INT5 vs INT8": INT5 is the MLX
+ *     default; the pages give no scale rule, grouping or layout, so the same
+ *     symmetric block-32 rule is read for it): Q = 15, codes in [-16, 15], 5-bit
+ *     two's complement.
+ *     A row of K codes is 5K/8 bytes: first K/2 bytes holding the low 4 bits of
+ *     every code (two per byte, low nibble = even k), then K/8 bytes holding
+ *     bit 4 of every code (code k in bit k%8 of byte k/8).
  *
  * The matmul is the plain definition over the dequantized weights, evaluated in
  * binary64 with a sequential loop over increasing k. Every product x*q*s is
@@ -127,13 +134,14 @@ double wqo_f64_from_f16_bits(uint16_t h)
 
 /* ------------------------------------------------------------------------ */
 /* Quantize + encode (the packing step).                                     */
-/* w: fp32 [N][K] row-major. q: int4 -> [N][K/2] bytes, int8 -> [N][K] bytes. */
+/* w: fp32 [N][K] row-major. q: int4 -> [N][K/2] bytes, int5 -> [N][5K/8],    */
+/* int8 -> [N][K] bytes.                                                     */
 /* scales: binary16 bits [N][K/32].                                          */
 /* ------------------------------------------------------------------------ */
 static void quantize_block(const float *w, int bits, int8_t codes[QBLOCK], uint16_t *scale_bits)
 {
-    const int Qmax = (bits == 4) ? 7 : 127;
-    const int lo = (bits == 4) ? -8 : -128;
+    const int Qmax = (bits == 4) ? 7 : (bits == 5) ? 15 : 127;
+    const int lo = -Qmax - 1;
     const int hi = Qmax;
 
     /* 1. largest magnitude in the block (exact in fp32) */
@@ -171,12 +179,19 @@ void wqo_quantize(const float *w, int64_t N, int64_t K, int bits, uint8_t *q, ui
         for (int64_t b = 0; b < nb; ++b) {
             int8_t codes[QBLOCK];
             quantize_block(w + n * K + b * QBLOCK, bits, codes, &scales[n * nb + b]);
-            if (bits == 4) {
-                uint8_t *dst = q + n * (K / 2) + b * (QBLOCK / 2);
+            if (bits == 4 || bits == 5) {
+                const int64_t row = (bits == 4) ? K / 2 : K / 2 + K / 8;
+                uint8_t *dst = q + n * row + b * (QBLOCK / 2);
                 for (int j = 0; j < QBLOCK / 2; ++j) {
                     const uint8_t even = (uint8_t)codes[2 * j] & 0x0Fu;
                     const uint8_t odd = (uint8_t)codes[2 * j + 1] & 0x0Fu;
                     dst[j] = (uint8_t)(even | (odd << 4));
+                }
+                if (bits == 5) {
+                    uint8_t *hb = q + n * row + K / 2 + b * (QBLOCK / 8);
+                    for (int j = 0; j < QBLOCK / 8; ++j) hb[j] = 0;
+                    for (int i = 0; i < QBLOCK; ++i)
+                        hb[i / 8] |= (uint8_t)((((uint8_t)codes[i] >> 4) & 1u) << (i % 8));
                 }
             } else {
                 uint8_t *dst = q + n * K + b * QBLOCK;
@@ -187,7 +202,7 @@ void wqo_quantize(const float *w, int64_t N, int64_t K, int bits, uint8_t *q, ui
 }
 
 /* ------------------------------------------------------------------------ */
-/* Decode one code (two's complement nibble or byte).                        */
+/* Decode one code (two's complement nibble, 5-bit field or byte).           */
 /* ------------------------------------------------------------------------ */
 static int code_at(const uint8_t *q, int64_t K, int bits, int64_t n, int64_t k)
 {
@@ -195,6 +210,13 @@ static int code_at(const uint8_t *q, int64_t K, int bits, int64_t n, int64_t k)
         const uint8_t byte = q[n * (K / 2) + k / 2];
         const int t = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
         return (t >= 8) ? t - 16 : t;
+    }
+    if (bits == 5) {
+        const uint8_t *row = q + n * (K / 2 + K / 8);
+        const uint8_t byte = row[k / 2];
+        const int lo4 = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+        const int t = lo4 | (((row[K / 2 + k / 8] >> (k % 8)) & 1) << 4);
+        return (t >= 16) ? t - 32 : t;
     }
     const uint8_t byte = q[n * K + k];
     return (byte >= 128) ? (int)byte - 256 : (int)byte;

@@ -77,8 +77,8 @@ def quantize_block_exact(w, bits: int):
     Returns (codes list, scale as Fraction). Mirrors the stated rule only:
     scale = binary16(binary32(amax / Q)); code = clamp(rne(binary32(w / scale))).
     """
-    Q = 7 if bits == 4 else 127
-    lo, hi = (-8, 7) if bits == 4 else (-128, 127)
+    Q = {4: 7, 5: 15, 8: 127}[bits]
+    lo, hi = -Q - 1, Q
     ws = [f32_frac(v) for v in w]
     amax = max(abs(v) for v in ws)
     s32 = round_f32(amax / Q)
@@ -90,6 +90,11 @@ def quantize_block_exact(w, bits: int):
         r = round_f32(v / s16)
         codes.append(min(hi, max(lo, rne_int(r))))
     return codes, s16
+
+
+def signed5(t: int) -> int:
+    """The unique v in [-16, 15] congruent to t modulo 32."""
+    return [v for v in range(-16, 16) if (v - t) % 32 == 0][0]
 
 
 def signed_nibble(t: int) -> int:

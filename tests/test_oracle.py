@@ -100,6 +100,7 @@ def test_f16_roundtrip_values(oracle_mod):
 @pytest.mark.parametrize("name,bits,unit", [
     ("int4_block_worked_example.txt", 4, 2.0 ** -7),
     ("int8_block_worked_example.txt", 8, 2.0 ** -8),
+    ("int5_block_worked_example.txt", 5, 2.0 ** -7),
 ])
 def test_worked_examples(oracle_mod, name, bits, unit):
     w_mult, codes, scale, packed = _read_golden(name)
@@ -135,10 +136,22 @@ def test_non_dyadic_scale(oracle_mod):
     assert wh == 0.999755859375
 
 
+def test_non_dyadic_scale_int5(oracle_mod):
+    """int5: s32 = fl32(1/15), s16 = 0x2C44 = 2^-4 + 68 * 2^-14, code 15."""
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, 69] = 1.0
+    q, s = oracle_mod.quantize(w, 5)
+    assert s[0].tolist() == [0, 0, 0x2C44, 0]
+    assert exact.f16_value(0x2C44) == Fraction(1, 16) + Fraction(68, 2 ** 14)
+    codes = oracle_mod.decode(q, 128, 5)[0]
+    assert codes[69] == 15 and np.count_nonzero(codes) == 1
+    assert oracle_mod.dequant(q, s, 128, 5)[0, 69] == 0.999755859375
+
+
 def _crafted_blocks(bits):
     """Blocks whose scale is an exact binary16 value and whose ratios w/s hit
     exact half-integers and their binary32 neighbours."""
-    Q = 7 if bits == 4 else 127
+    Q = {4: 7, 5: 15, 8: 127}[bits]
     rows = []
     rng = inputs.generator((99, bits))
     for s_bits in [0x2000, 0x1C00, 0x3092, 0x2155, 0x0001, 0x03FF, 0x0400, 0x1FFF, 0x5000]:
@@ -160,7 +173,7 @@ def _crafted_blocks(bits):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 def test_quantizer_vs_exact_rational(oracle_mod, bits):
     """Scale bits and every code equal an exact-rational evaluation of the rule."""
     w = _crafted_blocks(bits)
@@ -172,12 +185,12 @@ def test_quantizer_vs_exact_rational(oracle_mod, bits):
         assert codes[i].tolist() == want_codes, i
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 def test_quantizer_invariants(oracle_mod, bits):
     """On N(0, 0.02) weights: every non-zero block reaches +-Q, codes stay in
     [-Q, Q], the reconstruction error is at most half a scale, and packing the
     dequantized weights again reproduces the same bytes."""
-    Q = 7 if bits == 4 else 127
+    Q = {4: 7, 5: 15, 8: 127}[bits]
     w = inputs.normal((512, 1024), seed=(7, bits), sigma=0.02)
     q, s = oracle_mod.quantize(w, bits)
     codes = oracle_mod.decode(q, 1024, bits).astype(np.int64).reshape(512, 32, 32)
@@ -207,6 +220,27 @@ def test_decode_table(oracle_mod):
     assert oracle_mod.decode(np.full((1, 32), 0x80, np.uint8), 32, 8).tolist() == [[-128] * 32]
 
 
+def test_decode_table_int5(oracle_mod):
+    """int5 rows (K/2 bytes of low nibbles, then K/8 bytes of bit 4): every one of
+    the 32 five-bit fields, placed at every position, decodes to its
+    two's-complement value; all-ones gives -1 and nibble 0 with bit 4 gives -16."""
+    K = 32
+    rows = []
+    want = []
+    for shift in range(32):
+        fields = [(k + shift) % 32 for k in range(K)]
+        nib = bytes((fields[2 * j] & 15) | ((fields[2 * j + 1] & 15) << 4) for j in range(K // 2))
+        hb = bytes(sum(((fields[8 * j + i] >> 4) & 1) << i for i in range(8)) for j in range(K // 8))
+        rows.append(np.frombuffer(nib + hb, dtype=np.uint8))
+        want.append([exact.signed5(f) for f in fields])
+    c5 = oracle_mod.decode(np.stack(rows), K, 5)
+    assert c5.tolist() == want
+    assert oracle_mod.decode(np.full((1, 20), 0xFF, np.uint8), 32, 5).tolist() == [[-1] * 32]
+    q = np.zeros((1, 20), np.uint8)
+    q[0, 16:] = 0xFF
+    assert oracle_mod.decode(q, 32, 5).tolist() == [[-16] * 32]
+
+
 # ---------------------------------------------------------------- matmul
 
 def _exact_dequant(q, s, K, bits):
@@ -219,6 +253,10 @@ def _exact_dequant(q, s, K, bits):
             if bits == 4:
                 byte = int(q[n, k // 2])
                 t = exact.signed_nibble(byte & 0xF if k % 2 == 0 else byte >> 4)
+            elif bits == 5:
+                byte = int(q[n, k // 2])
+                lo4 = byte & 0xF if k % 2 == 0 else byte >> 4
+                t = exact.signed5(lo4 | (((int(q[n, K // 2 + k // 8]) >> (k % 8)) & 1) << 4))
             else:
                 t = int(np.uint8(q[n, k]).view(np.int8))
             row.append(t * exact.f16_value(int(s[n, k // 32])))
@@ -226,7 +264,7 @@ def _exact_dequant(q, s, K, bits):
     return out
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 @pytest.mark.parametrize("M,K,N", [(1, 32, 1), (2, 64, 3), (3, 96, 5), (1, 96, 4), (3, 32, 2)])
 def test_matmul_exact_rational(oracle_mod, bits, M, K, N):
     """y equals the exact rational sum up to the binary64 summation bound."""
@@ -245,7 +283,7 @@ def test_matmul_exact_rational(oracle_mod, bits, M, K, N):
             assert abs(Fraction(B[m, n]) - be) <= K * Fraction(1, 2 ** 53) * be
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 def test_matmul_one_hot_readout(oracle_mod, bits):
     """x = e_k reads column k of the dequantized weights exactly, for every k."""
     K, N = 96, 7
@@ -260,7 +298,7 @@ def test_matmul_one_hot_readout(oracle_mod, bits):
             assert Fraction(y[k, n]) == wh[n][k]
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 def test_matmul_zero_scale_row_and_signs(oracle_mod, bits):
     K, N, M = 64, 5, 3
     w = inputs.normal((N, K), seed=(14, bits), sigma=0.02)
@@ -277,7 +315,7 @@ def test_matmul_zero_scale_row_and_signs(oracle_mod, bits):
     assert np.array_equal(y8, 8 * y1)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 def test_matmul_linearity_and_library(oracle_mod, bits):
     """Linear in x within the binary64 bound, and equal to a library fp64 matmul
     over the dequantized weights within the same bound."""
@@ -328,11 +366,15 @@ def test_embed_worked_examples(oracle_mod):
     """A table built from the two worked examples: each looked-up row is the
     example's codes times its scale (2^-7, 2^-8), exactly; a zero row stays
     zero; the row whose only weight is 1.0 (k = 5) reads 7 * 0x3092 =
-    0.999755859375 for int4 and 127 * (2^-7 + 2^-14) = 0.99993896484375 for int8
-    (1/127 rounds to 2^-7 + 2^-14 in binary16); ids outside the table give NaN rows."""
+    0.999755859375 for int4, 15 * 0x2C44 = 15 * (2^-4 + 68 * 2^-14) =
+    0.999755859375 for int5 and 127 * (2^-7 + 2^-14) = 0.99993896484375 for int8
+    (1/15 and 1/127 round to those binary16 values); ids outside the table give
+    NaN rows."""
     w4, c4, _, _ = _read_golden("int4_block_worked_example.txt")
+    w5, c5, _, _ = _read_golden("int5_block_worked_example.txt")
     w8, c8, _, _ = _read_golden("int8_block_worked_example.txt")
     for bits, w_mult, codes, unit, one in ((4, w4, c4, 2.0 ** -7, 0.999755859375),
+                                           (5, w5, c5, 2.0 ** -7, 0.999755859375),
                                            (8, w8, c8, 2.0 ** -8, 0.99993896484375)):
         w = np.zeros((3, 64), dtype=np.float32)
         w[0, :32] = np.array(w_mult) * unit
@@ -347,7 +389,7 @@ def test_embed_worked_examples(oracle_mod):
         assert np.isnan(e[4]).all() and np.isnan(e[5]).all()
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [4, 5, 8])
 def test_embed_equals_one_hot_readout(oracle_mod, bits):
     """Looking up row n equals reading column n of the matmul with x = I
     (the matmul is a separate routine of the oracle: y[k, n] = w^[n, k])."""
