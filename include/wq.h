@@ -1,5 +1,5 @@
 /*
- * wq.h -- weight-only block-32 int4/int8 matmul for AMD MI355X (gfx950).
+ * wq.h -- weight-only block-32 int4/int5/int8 matmul for AMD MI355X (gfx950).
  *
  * The operation (TinyMOSS-Diarize devpost page, "How we built it": strictly
  * weight-only kernels, FP32 activations, dequantization fused into the matmul,
@@ -14,6 +14,13 @@
  *   y       fp32  [M][N]            (overwritten; no bias, no accumulate)
  *   q int4  uint8 [N][K/2]          two codes per byte, low nibble = even k,
  *                                   two's complement, codes in [-8, 7]
+ *   q int5  uint8 [N][5K/8]         per row: K/2 bytes of the low 4 bits of every
+ *                                   code as for int4, then K/8 bytes of bit 4 of
+ *                                   every code (code k in bit k%8 of byte k/8);
+ *                                   5-bit two's complement, codes in [-16, 15].
+ *                                   (INT5 is the MLX default of the soniqo MOSS
+ *                                   guide, "INT5 vs INT8"; the pages give no
+ *                                   layout or scale rule, this is the library's.)
  *   q int8  int8  [N][K]            two's complement, codes in [-128, 127]
  *   scales  binary16 bits [N][K/32] one scale per 32 consecutive k
  *
@@ -22,7 +29,8 @@
  *     caller; the library allocates nothing and keeps no state.
  *   - Arguments are validated on the host before any launch; a non-zero
  *     wq_status is returned and nothing is launched. Requirements: bits in
- *     {4, 8}; K > 0 and K % 32 == 0; N >= 0; M >= 0; non-null pointers for
+ *     {4, 5, 8}; K > 0 and K % 32 == 0 (K % 128 == 0 for int5, so rows stay
+ *     16-byte aligned); N >= 0; M >= 0; non-null pointers for
  *     non-empty calls; x, y, q, scales 16-byte aligned. y must not alias an
  *     input.
  *   - Empty calls (M == 0 or N == 0) return WQ_OK without launching.
@@ -44,8 +52,8 @@ extern "C" {
 enum wq_status {
     WQ_OK = 0,
     WQ_ERR_NULL = 1,      /* a required pointer is null */
-    WQ_ERR_SHAPE = 2,     /* K <= 0, K % 32 != 0, negative M or N, or too large */
-    WQ_ERR_BITS = 3,      /* bits not 4 or 8 */
+    WQ_ERR_SHAPE = 2,     /* K <= 0, K % 32 != 0 (int5: K % 128 != 0), negative M or N, or too large */
+    WQ_ERR_BITS = 3,      /* bits not 4, 5 or 8 */
     WQ_ERR_ALIGN = 4,     /* a pointer or table offset is misaligned */
     WQ_ERR_M_RANGE = 5,   /* M outside the entry point's range (wq_gemv: 1..16) */
     WQ_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
@@ -66,9 +74,9 @@ size_t wq_s_bytes(int64_t N, int64_t K);
  * Per row n and block b of 32 consecutive k (the block-32 symmetric scheme of
  * the pages above; the scale rule and rounding are this library's reading):
  *   amax = max |w|;  s = binary16_rne(amax / Q) with fp32 division,
- *   Q = 7 (int4) or 127 (int8);  if s == 0 every code is 0;
- *   else q = clamp(round_half_even(w / s), lo, hi) with fp32 division by the
- *   stored binary16 scale, (lo, hi) = (-8, 7) or (-128, 127).
+ *   Q = 7 (int4), 15 (int5) or 127 (int8);  if s == 0 every code is 0;
+ *   else q = clamp(round_half_even(w / s), -Q-1, Q) with fp32 division by the
+ *   stored binary16 scale.
  * Inputs must be finite with amax / Q <= 65504 (not checked here).
  * Output is bit-exact: one correct result exists for every input.
  */

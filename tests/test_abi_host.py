@@ -27,23 +27,27 @@ def test_exports_every_header_symbol(lib):
             "wq_embed", "wq_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.wq_abi_version() == 2
+    assert lib.wq_abi_version() == 3
 
 
 def test_sizes(lib):
     assert lib.wq_q_bytes(2048, 1024, 4) == 2048 * 512
     assert lib.wq_q_bytes(151936, 1024, 8) == 151936 * 1024
     assert lib.wq_s_bytes(2048, 1024) == 2048 * 32 * 2
-    assert lib.wq_q_bytes(10, 33, 4) == 0 and lib.wq_q_bytes(10, 32, 5) == 0
+    assert lib.wq_q_bytes(10, 33, 4) == 0 and lib.wq_q_bytes(10, 32, 6) == 0
+    # int5: 5K/8 bytes per row, K % 128 == 0
+    assert lib.wq_q_bytes(10, 128, 5) == 800 and lib.wq_q_bytes(10, 96, 5) == 0
 
 
 @pytest.mark.parametrize("fn", ["wq_gemv", "wq_gemm", "wq_linear"])
 def test_matmul_validation(lib, fn):
     f = getattr(lib, fn)
     # bits
-    assert f(FAKE, 1, 32, 8, 5, FAKE, FAKE, FAKE, None) == BITS
+    assert f(FAKE, 1, 32, 8, 6, FAKE, FAKE, FAKE, None) == BITS
     # shapes
     assert f(FAKE, 1, 33, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 1, 96, 8, 5, FAKE, FAKE, FAKE, None) == SHAPE      # int5 needs K % 128 == 0
+    assert f(None, 1, 128, 8, 5, FAKE, FAKE, FAKE, None) == NULL      # int5 accepted
     assert f(FAKE, 1, 0, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, -1, 32, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, 1, 32, -8, 4, FAKE, FAKE, FAKE, None) == SHAPE
@@ -69,6 +73,8 @@ def test_gemv_m_range(lib):
 
 def test_pack_unpack_validation(lib):
     assert lib.wq_pack(FAKE, 4, 32, 3, FAKE, FAKE, None) == BITS
+    assert lib.wq_pack(FAKE, 4, 32, 5, FAKE, FAKE, None) == SHAPE
+    assert lib.wq_pack(None, 4, 128, 5, FAKE, FAKE, None) == NULL
     assert lib.wq_pack(FAKE, 4, 48, 4, FAKE, FAKE, None) == SHAPE
     assert lib.wq_pack(None, 4, 32, 4, FAKE, FAKE, None) == NULL
     assert lib.wq_pack(FAKE, 4, 32, 4, MIS, FAKE, None) == ALIGN
@@ -79,7 +85,7 @@ def test_pack_unpack_validation(lib):
 
 def test_embed_validation(lib):
     f = lib.wq_embed
-    assert f(FAKE, 4, 32, 8, 5, FAKE, FAKE, FAKE, None) == BITS
+    assert f(FAKE, 4, 32, 8, 6, FAKE, FAKE, FAKE, None) == BITS
     assert f(FAKE, 4, 48, 8, 8, FAKE, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, -1, 32, 8, 8, FAKE, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, 4, 32, -8, 8, FAKE, FAKE, FAKE, None) == SHAPE

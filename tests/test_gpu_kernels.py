@@ -35,7 +35,7 @@ def _crafted(N, K, bits, seed):
     nb = K // 32
     mags = np.float32(10.0) ** rng.uniform(-9, 2, size=(N, nb)).astype(np.float32)
     w = (w.reshape(N, nb, 32) * mags[:, :, None]).reshape(N, K)
-    Q = 7 if bits == 4 else 127
+    Q = {4: 7, 5: 15, 8: 127}[bits]
     for n in range(N):
         b = int(rng.integers(0, nb))
         w[n, 32 * b: 32 * b + 32] = 0                     # a zero block per row

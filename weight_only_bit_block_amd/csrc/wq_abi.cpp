@@ -16,7 +16,10 @@ constexpr int64_t kMaxK = (int64_t)1 << 24;
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-inline int check_bits(int bits) { return (bits == 4 || bits == 8) ? WQ_OK : WQ_ERR_BITS; }
+inline int check_bits(int bits) { return (bits == 4 || bits == 5 || bits == 8) ? WQ_OK : WQ_ERR_BITS; }
+
+// int5 rows are 5K/8 bytes; K % 128 == 0 keeps every row 16-byte aligned.
+inline int check_row(int64_t K, int bits) { return (bits == 5 && K % 128 != 0) ? WQ_ERR_SHAPE : WQ_OK; }
 
 inline int check_shape(int64_t M, int64_t K, int64_t N)
 {
@@ -34,6 +37,8 @@ int check_matmul(const float *x, int64_t M, int64_t K, int64_t N, int bits, cons
     int st = check_bits(bits);
     if (st) return st;
     st = check_shape(M, K, N);
+    if (st) return st;
+    st = check_row(K, bits);
     if (st) return st;
     if (M == 0 || N == 0) { *empty = true; return WQ_OK; }
     if (!x || !q || !scales || !y) return WQ_ERR_NULL;
@@ -67,7 +72,7 @@ extern "C" {
 
 size_t wq_q_bytes(int64_t N, int64_t K, int bits)
 {
-    if (check_bits(bits) || check_shape(0, K, N)) return 0;
+    if (check_bits(bits) || check_shape(0, K, N) || check_row(K, bits)) return 0;
     return (size_t)N * (size_t)K * (size_t)bits / 8;
 }
 
@@ -84,6 +89,8 @@ int wq_pack(const float *w, int64_t N, int64_t K, int bits, void *q, uint16_t *s
     if (st) return st;
     st = check_shape(0, K, N);
     if (st) return st;
+    st = check_row(K, bits);
+    if (st) return st;
     if (N == 0) return WQ_OK;
     if (!w || !q || !scales) return WQ_ERR_NULL;
     if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 16)) return WQ_ERR_ALIGN;
@@ -95,6 +102,8 @@ int wq_unpack(const void *q, int64_t N, int64_t K, int bits, int8_t *codes, hipS
     int st = check_bits(bits);
     if (st) return st;
     st = check_shape(0, K, N);
+    if (st) return st;
+    st = check_row(K, bits);
     if (st) return st;
     if (N == 0) return WQ_OK;
     if (!q || !codes) return WQ_ERR_NULL;
@@ -138,6 +147,8 @@ int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits, 
     if (st) return st;
     st = check_shape(n_ids, K, N);
     if (st) return st;
+    st = check_row(K, bits);
+    if (st) return st;
     if (n_ids == 0) return WQ_OK;
     if (!ids || !out) return WQ_ERR_NULL;
     if (N > 0 && (!q || !scales)) return WQ_ERR_NULL;
@@ -167,6 +178,8 @@ int wq_table_layout(wq_desc *table, int count, uint64_t *package_bytes)
         if (st) return st;
         st = check_shape(0, d.K, d.N);
         if (st) return st;
+        st = check_row(d.K, d.bits);
+        if (st) return st;
         d.q_off = align64(cur);
         cur = d.q_off + (uint64_t)d.N * (uint64_t)d.K * (uint64_t)d.bits / 8;
         d.s_off = align64(cur);
@@ -187,6 +200,8 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
         int st = check_bits(d.bits);
         if (st) return st;
         st = check_shape(M, d.K, d.N);
+        if (st) return st;
+        st = check_row(d.K, d.bits);
         if (st) return st;
         st = gemv_offsets_ok(d.K, d.N, d.bits);
         if (st) return st;
@@ -225,7 +240,7 @@ const char *wq_strerror(int status)
     case WQ_OK: return "ok";
     case WQ_ERR_NULL: return "null pointer argument";
     case WQ_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 32; M, N >= 0; sizes in range)";
-    case WQ_ERR_BITS: return "bits must be 4 or 8";
+    case WQ_ERR_BITS: return "bits must be 4, 5 or 8";
     case WQ_ERR_ALIGN: return "misaligned pointer or table offset";
     case WQ_ERR_M_RANGE: return "M outside the range of this entry point";
     case WQ_ERR_HIP: return "HIP runtime error at launch";
@@ -234,6 +249,6 @@ const char *wq_strerror(int status)
     }
 }
 
-int wq_abi_version(void) { return 2; }
+int wq_abi_version(void) { return 3; }
 
 }  // extern "C"

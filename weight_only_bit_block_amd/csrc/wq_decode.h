@@ -1,4 +1,4 @@
-// wq_decode.h -- in-register unpack of packed int4 / int8 codes to exact binary16.
+// wq_decode.h -- in-register unpack of packed int4 / int5 / int8 codes to exact binary16.
 //
 // A code c (two's complement) is first turned into offset form c + 8 (int4) or
 // c + 128 (int8) by flipping its top bit; ORing that field into the mantissa of
@@ -98,13 +98,66 @@ __device__ __forceinline__ h8 unpack8_int8(uint32_t d0, uint32_t d1, const Decod
     return r;
 }
 
+// int5 (codes in [-16, 15]): a dword of low nibbles as in int4 (unsigned low 4
+// bits of codes k0..k7) and a byte whose bit i is bit 4 of code k_i. The nibble
+// is taken as is and NOT(bit 4) goes into the mantissa bit above it, so each
+// half holds 1024 + (k + 16) (or 1024 + 16 (k + 16) for the odd nibbles), and
+// one packed fp16 subtract (or FMA) recovers k exactly.
+struct Decode5Consts {
+    uint32_t m_lo, m_hi;   // nibbles 0 and 4, 1 and 5
+    uint32_t k;            // 0x6400 magic in both halves
+    uint32_t b0, b1, b2, b3;
+    __device__ __forceinline__ static Decode5Consts make()
+    {
+        Decode5Consts c;
+        c.m_lo = vgpr(0x000F000Fu);
+        c.m_hi = vgpr(0x00F000F0u);
+        c.k = vgpr(0x64006400u);
+        c.b0 = vgpr(0x00010001u);
+        c.b1 = vgpr(0x00020002u);
+        c.b2 = vgpr(0x00040004u);
+        c.b3 = vgpr(0x00080008u);
+        return c;
+    }
+};
+
+// -> exact fp16 pairs (k0,k4), (k1,k5), (k2,k6), (k3,k7), as decode_int4.
+__device__ __forceinline__ void decode_int5(uint32_t d, uint32_t hbyte, const Decode5Consts &c, h2 &p04,
+                                            h2 &p15, h2 &p26, h2 &p37)
+{
+    const uint32_t nh = ~hbyte;
+    const uint32_t t = (nh & 0xFu) | ((nh & 0xF0u) << 12);   // NOT bit 4 of k0..k3 in bits 0-3, k4..k7 in 16-19
+    const uint32_t v = d >> 8;
+    const h2 a = as_h2((d & c.m_lo) | ((t & c.b0) << 4) | c.k);   // 1024 + (k + 16)
+    const h2 b = as_h2((d & c.m_hi) | ((t & c.b1) << 7) | c.k);   // 1024 + 16 (k + 16)
+    const h2 e = as_h2((v & c.m_lo) | ((t & c.b2) << 2) | c.k);
+    const h2 f = as_h2((v & c.m_hi) | ((t & c.b3) << 5) | c.k);
+    const h2 off = {(_Float16)1040.0f, (_Float16)1040.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off16 = {(_Float16)80.0f, (_Float16)80.0f};
+    p04 = a - off;
+    p15 = b * sixteenth - off16;
+    p26 = e - off;
+    p37 = f * sixteenth - off16;
+}
+
+__device__ __forceinline__ h8 unpack8_int5(uint32_t d, uint32_t hbyte, const Decode5Consts &c)
+{
+    h2 a, b, e, f;
+    decode_int5(d, hbyte, c, a, b, e, f);
+    h8 r;
+    r[0] = a.x; r[1] = a.y; r[2] = b.x; r[3] = b.y;
+    r[4] = e.x; r[5] = e.y; r[6] = f.x; r[7] = f.y;
+    return r;
+}
+
 // Position of k (0..7) within an 8-group in the operand order above.
 template <int BITS>
 __device__ __forceinline__ constexpr int operand_slot(int k)
 {
-    // int4: k0->0 k4->1 k1->2 k5->3 k2->4 k6->5 k3->6 k7->7
-    // int8: k0->0 k2->1 k1->2 k3->3 k4->4 k6->5 k5->6 k7->7
-    return BITS == 4 ? ((k & 3) * 2 + (k >> 2)) : ((k & 4) + (k & 1) * 2 + ((k >> 1) & 1));
+    // int4 and int5: k0->0 k4->1 k1->2 k5->3 k2->4 k6->5 k3->6 k7->7
+    // int8:          k0->0 k2->1 k1->2 k3->3 k4->4 k6->5 k5->6 k7->7
+    return BITS != 8 ? ((k & 3) * 2 + (k >> 2)) : ((k & 4) + (k & 1) * 2 + ((k >> 1) & 1));
 }
 
 }  // namespace wq

@@ -7,7 +7,9 @@
 // tokens. Here that table is the packed block-32 lm_head itself: row ids[i] is
 // decoded and scaled into out[i] in fp32 and no dequantized table is ever stored.
 // code * scale is exact in fp32 (a binary16 scale has 11 significant bits, a
-// code at most 8), so every output is the exact dequantized weight.
+// code at most 8), so every output is the exact dequantized weight. int4, int5
+// and int8 tables are accepted (int5: a row's low-nibble plane, then its bit-4
+// plane).
 //
 // One thread per 8 consecutive values of an output row: consecutive threads
 // read consecutive code bytes of a row and write consecutive 32-byte pieces of
@@ -50,6 +52,16 @@ __global__ __launch_bounds__(kEmbedThreads) void embed_kernel(const int32_t *__r
             c[j] = (int)(int8_t)(v.x >> (8 * j));
             c[4 + j] = (int)(int8_t)(v.y >> (8 * j));
         }
+    } else if constexpr (BITS == 5) {
+        // the row's low-nibble plane, then its bit-4 plane
+        const uint8_t *row = q + id * (int64_t)(K / 2 + K / 8);
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(row + (k0 >> 1));
+        const uint32_t hb = row[(K >> 1) + (k0 >> 3)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t f = ((v >> (4 * j)) & 0xFu) | (((hb >> j) & 1u) << 4);
+            c[j] = (int)(f << 27) >> 27;                                       // 5-bit field, sign-extended
+        }
     } else {
         const uint32_t v = *reinterpret_cast<const uint32_t *>(q + id * (int64_t)(K >> 1) + (k0 >> 1));
 #pragma unroll
@@ -68,6 +80,8 @@ hipError_t launch_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N,
     const unsigned grid = (unsigned)((groups + kEmbedThreads - 1) / kEmbedThreads);
     if (bits == 4)
         embed_kernel<4><<<grid, kEmbedThreads, 0, stream>>>(ids, (int)K, N, (const uint8_t *)q, scales, out, groups);
+    else if (bits == 5)
+        embed_kernel<5><<<grid, kEmbedThreads, 0, stream>>>(ids, (int)K, N, (const uint8_t *)q, scales, out, groups);
     else
         embed_kernel<8><<<grid, kEmbedThreads, 0, stream>>>(ids, (int)K, N, (const uint8_t *)q, scales, out, groups);
     return hipGetLastError();

@@ -1,4 +1,4 @@
-// wq_gemm.hip -- prefill GEMM for block-32 int4 / int8 weights (any M, tuned for M >= 128).
+// wq_gemm.hip -- prefill GEMM for block-32 int4 / int5 / int8 weights (any M, tuned for M >= 128).
 //
 // The TinyMOSS-Diarize devpost page ("How we built it") describes a blocked
 // prefill GEMM that unpacks each weight group once and reuses it across all
@@ -52,15 +52,17 @@ constexpr int kXcds = 8;
 // LDS layout of one stage buffer (BM rows per workgroup tile; 64 as launched).
 //   A: x as binary16, [BM rows][KT*32 values]; row pitch 128 bytes, 16-byte
 //      slot s of row r stored at slot s ^ ((r >> 1) & 7).
-//   B: packed codes, [BN columns][KT * CB bytes].
+//   B: packed codes, [BN columns][KT * CB bytes] (int5: the low nibbles).
+//   H: int5 only, bit 4 of the codes, [BN columns][KT dwords].
 //   S: binary16 scales, [BN columns][KT].
 template <int BITS, int BM>
 struct Stage {
-    static constexpr int CB = BITS * 4;                    // code bytes per column per block
+    static constexpr int CB = BITS == 8 ? 32 : 16;         // code bytes per column per block (int5: nibbles)
     static constexpr int A_BYTES = BM * KT * 64;
     static constexpr int B_BYTES = BN * KT * CB;
+    static constexpr int H_BYTES = BITS == 5 ? BN * KT * 4 : 0;   // int5: bit 4 of the codes
     static constexpr int S_BYTES = BN * KT * 2;
-    static constexpr int BYTES = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int BYTES = A_BYTES + B_BYTES + H_BYTES + S_BYTES;
 };
 
 __device__ __forceinline__ int aslot(int r, int s) { return r * (KT * 4) + (s ^ ((r >> 1) & 7)); }
@@ -103,6 +105,8 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     const int st0 = h * NTh;                     // its first stage
     uint8_t *const lds = lds_all + h * 2 * L::BYTES;
     const DecodeConsts dc = DecodeConsts::make();
+    Decode5Consts dc5;
+    if constexpr (BITS == 5) dc5 = Decode5Consts::make();
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)M * K * 4);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint64_t)N * C * 2);
@@ -143,6 +147,8 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     f4 xv[XI][2];
     u4 qv[QI];
     uint16_t sv[KT];
+    uint32_t hv[KT];                              // int5: bit-4 dwords of column sn
+    const uint32_t hoff = (uint32_t)sn * qrow + (uint32_t)K / 2;
     auto issue = [&](int st) {
         const int b0 = (st0 + st) * KT;
 #pragma unroll
@@ -163,6 +169,7 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
         for (int k = 0; k < KT; ++k) {
             const int b = b0 + k < C ? b0 + k : C - 1;
             sv[k] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff + (uint32_t)b * 2, 0, 0);
+            if constexpr (BITS == 5) hv[k] = __builtin_amdgcn_raw_buffer_load_b32(qr, hoff + (uint32_t)b * 4, 0, 0);
         }
     };
     // x rounded to binary16 in operand order, the codes and the scales (zero past
@@ -181,10 +188,15 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
             *reinterpret_cast<h8 *>(base + xlds[i]) = h;
         }
         if (t < BN) {
-            uint16_t *Sc = reinterpret_cast<uint16_t *>(base + L::A_BYTES + L::B_BYTES);
+            uint16_t *Sc = reinterpret_cast<uint16_t *>(base + L::A_BYTES + L::B_BYTES + L::H_BYTES);
             const int b0 = (st0 + st) * KT;
 #pragma unroll
             for (int k = 0; k < KT; ++k) Sc[t * KT + k] = b0 + k < C ? sv[k] : (uint16_t)0;
+            if constexpr (BITS == 5) {
+                uint32_t *H = reinterpret_cast<uint32_t *>(base + L::A_BYTES + L::B_BYTES);
+#pragma unroll
+                for (int k = 0; k < KT; ++k) H[t * KT + k] = hv[k];
+            }
         }
     };
 
@@ -220,7 +232,8 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
         const int cur = it & 1;
         const uint8_t *base = lds + cur * L::BYTES;
         const uint8_t *B = base + L::A_BYTES;
-        const uint16_t *Sc = reinterpret_cast<const uint16_t *>(B + L::B_BYTES);
+        const uint8_t *H = B + L::B_BYTES;
+        const uint16_t *Sc = reinterpret_cast<const uint16_t *>(H + L::H_BYTES);
 #pragma unroll
         for (int kb = 0; kb < KT; ++kb) {
             // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
@@ -229,8 +242,12 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
             const uint8_t *qp = B + c * (KT * CB) + kb * CB;
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                if (BITS == 4) {
+                if constexpr (BITS == 4) {
                     b[st] = unpack8_int4(*reinterpret_cast<const uint32_t *>(qp + (2 * st + g) * 4), dc);
+                } else if constexpr (BITS == 5) {
+                    // bit 4 of these 8 codes: byte 2*st+g of the block's dword
+                    const uint32_t hbyte = H[(c * KT + kb) * 4 + 2 * st + g];
+                    b[st] = unpack8_int5(*reinterpret_cast<const uint32_t *>(qp + (2 * st + g) * 4), hbyte, dc5);
                 } else {
                     const u2 v = *reinterpret_cast<const u2 *>(qp + (2 * st + g) * 8);
                     b[st] = unpack8_int8(v.x, v.y, dc);
@@ -331,6 +348,7 @@ hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
     if (bits == 4) return launch_shape<4>(x, M, K, N, q, scales, y, stream);
+    if (bits == 5) return launch_shape<5>(x, M, K, N, q, scales, y, stream);
     return launch_shape<8>(x, M, K, N, q, scales, y, stream);
 }
 

@@ -198,6 +198,49 @@ __device__ __forceinline__ void chunk_fma(const u4 (&w)[J], const uint8_t *const
         for (int m = 0; m < MT; ++m) acc[j][m] = __builtin_fmaf(sc[j], p0[j][m] + p1[j][m], acc[j][m]);
 }
 
+// int5 chunk: the int4 arithmetic above with the codes decoded from the chunk's
+// low nibbles and its 4 bytes of bit 4 (byte h covers codes 8h .. 8h+7).
+template <int MT, int J>
+__device__ __forceinline__ void chunk_fma5(const u4 (&w)[J], const uint32_t (&hb)[J], const uint8_t *const (&xp)[8],
+                                           int xstride, const Decode5Consts &dc, const float (&sc)[J],
+                                           float (&acc)[J][MT])
+{
+    float p0[J][MT], p1[J][MT];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) { p0[j][m] = 0.0f; p1[j][m] = 0.0f; }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        f4 xa[MT], xb[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            xa[m] = *reinterpret_cast<const f4 *>(xp[2 * h] + m * xstride);
+            xb[m] = *reinterpret_cast<const f4 *>(xp[2 * h + 1] + m * xstride);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            h2 t0, t1, t2, t3;
+            decode_int5(w[j][h], hb[j] >> (8 * h), dc, t0, t1, t2, t3);   // (k0,k4) (k1,k5) (k2,k6) (k3,k7)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                p0[j][m] = fmix(t0.x, xa[m].x, p0[j][m]);
+                p1[j][m] = fmix(t0.y, xb[m].x, p1[j][m]);
+                p0[j][m] = fmix(t1.x, xa[m].y, p0[j][m]);
+                p1[j][m] = fmix(t1.y, xb[m].y, p1[j][m]);
+                p0[j][m] = fmix(t2.x, xa[m].z, p0[j][m]);
+                p1[j][m] = fmix(t2.y, xb[m].z, p1[j][m]);
+                p0[j][m] = fmix(t3.x, xa[m].w, p0[j][m]);
+                p1[j][m] = fmix(t3.y, xb[m].w, p1[j][m]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[j][m] = __builtin_fmaf(sc[j], p0[j][m] + p1[j][m], acc[j][m]);
+}
+
 // The 8 x-piece pointers a lane reads for the chunk of block `blk` of a staged
 // segment, in the order its codes use them (int8: the chunk's half of the
 // block, pieces 4*half .. 4*half+3).
@@ -206,7 +249,7 @@ __device__ __forceinline__ void piece_ptrs(const uint8_t *xs, int blk, int half,
 {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int p = BITS == 4 ? k : half * 4 + (k & 3);
+        const int p = BITS != 8 ? k : half * 4 + (k & 3);
         xp[k] = xs + xslot(blk, p) * 16;
     }
 }
@@ -348,7 +391,10 @@ __device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, i
     const int C = K >> 5;
     const int CC = C * CPB;
     const uint32_t qrow = (uint32_t)K * BITS / 8;
+    const uint32_t hoff = (uint32_t)K / 2;      // int5: offset of the bit-4 plane in a row
     const DecodeConsts dc = DecodeConsts::make();
+    Decode5Consts dc5;
+    if constexpr (BITS == 5) dc5 = Decode5Consts::make();
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * qrow);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint64_t)N * C * 2);
     int64_t r = row0 + lrow;
@@ -376,7 +422,13 @@ __device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, i
                     _Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, rs + (uint32_t)(ch / CPB) * 2, 0, 0));
                 const uint8_t *xp[8];
                 piece_ptrs<BITS>(lds, ch / CPB - b0, ch & 1, xp);
-                chunk_fma<BITS, MT, 1>(wc, xp, nbs * 128, dc, sc, acc);
+                if constexpr (BITS == 5) {
+                    const uint32_t hb[1] = {
+                        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(qr, rq + hoff + (uint32_t)ch * 4, 0, kNonTemporal)};
+                    chunk_fma5<MT, 1>(wc, hb, xp, nbs * 128, dc5, sc, acc);
+                } else {
+                    chunk_fma<BITS, MT, 1>(wc, xp, nbs * 128, dc, sc, acc);
+                }
             }
         }
         reduce_store<MT, 1>(acc, G, li, row0 + lrow, N, mg, M, y);
@@ -405,15 +457,19 @@ __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint
     const int K = (int)d.K;
     const GemvGeom g = gemv_geom(K, BITS, d.N, true);
     const int64_t row0 = item * g.rows;
-    switch (g.kind) {
-    case kGemvJ2S2: gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
-    case kGemvJ1S2: gemv_item_fast<BITS, MT, 1, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
-    case kGemvJ1S4: gemv_item_fast<BITS, MT, 1, 4, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
-    case kGemvJ1S6:
-    case kGemvJ1S8:
-        gemv_item_fast<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
-        break;
-    default: gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds); break;
+    if constexpr (BITS == 5) {
+        gemv_item_general<5, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
+    } else {
+        switch (g.kind) {
+        case kGemvJ2S2: gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
+        case kGemvJ1S2: gemv_item_fast<BITS, MT, 1, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
+        case kGemvJ1S4: gemv_item_fast<BITS, MT, 1, 4, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
+        case kGemvJ1S6:
+        case kGemvJ1S8:
+            gemv_item_fast<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+            break;
+        default: gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds); break;
+        }
     }
 }
 
@@ -438,6 +494,7 @@ __global__ __launch_bounds__(kGemvThreads, (grouped_waves_per_simd<MT, MLOOP>())
     const uint8_t *q = base + d.q_off;
     const uint16_t *s = reinterpret_cast<const uint16_t *>(base + d.s_off);
     if (d.bits == 4) grouped_item<4, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
+    else if (d.bits == 5) grouped_item<5, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
     else grouped_item<8, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
 }
 
@@ -456,13 +513,17 @@ hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const
                           const uint16_t *s, float *y, hipStream_t stream)
 {
     const GemvGeom g = gemv_geom(K, BITS, N, false);
-    switch (g.kind) {
-    case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
-    case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
-    case kGemvJ1S4: return launch_kind<BITS, MT, 1, 4, MLOOP>(x, M, K, N, q, s, y, g, stream);
-    case kGemvJ1S6:
-    case kGemvJ1S8: return launch_kind<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(x, M, K, N, q, s, y, g, stream);
-    default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
+    if constexpr (BITS == 5) {
+        return launch_kind<5, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
+    } else {
+        switch (g.kind) {
+        case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        case kGemvJ1S4: return launch_kind<BITS, MT, 1, 4, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        case kGemvJ1S6:
+        case kGemvJ1S8: return launch_kind<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        }
     }
 }
 
@@ -494,6 +555,7 @@ hipError_t launch_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
     if (bits == 4) return launch_gemv_bits<4>(x, M, K, N, q, scales, y, stream);
+    if (bits == 5) return launch_gemv_bits<5>(x, M, K, N, q, scales, y, stream);
     return launch_gemv_bits<8>(x, M, K, N, q, scales, y, stream);
 }
 

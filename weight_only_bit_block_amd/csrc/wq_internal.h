@@ -21,6 +21,9 @@ constexpr int kWave = 64;           // gfx950 wavefront size
 // them), so the lanes of a row read G*16 contiguous bytes per load. A
 // workgroup item is IROWS = 4 * (64/G) * J consecutive rows of one tensor.
 //
+// int5 rows (the low-nibble plane, then the bit-4 plane) are read as int4
+// chunks plus the chunk's 4 bytes of bit 4, in the general form.
+//
 // Fast form (G == 16 and K % 256 == 0: every shape of the decoder): a lane owns
 // J rows and holds S of its chunks per row in registers at a time; the row is
 // walked in CPL/S segments of S chunks (S divides CPL). General form (any K %
@@ -58,7 +61,7 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
     g.J = 1;
     g.S = 1;
     g.kind = kGemvGeneral;
-    if (G == 16 && K % 256 == 0) {
+    if (G == 16 && K % 256 == 0 && bits != 5) {
         const int64_t rows_j2 = (int64_t)kGemvWaves * 4 * 2;
         if (g.CPL == 2) {
             const bool few = !grouped && (N + rows_j2 - 1) / rows_j2 < 256;

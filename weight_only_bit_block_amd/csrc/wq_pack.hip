@@ -1,12 +1,16 @@
-// wq_pack.hip -- quantize + pack, and unpack, for block-32 int4 / int8 codes.
+// wq_pack.hip -- quantize + pack, and unpack, for block-32 int4 / int5 / int8 codes.
 //
 // The block-32 symmetric scheme is the one the pages describe for the MOSS
 // decoder (moss-transcribe-diarize-litert card, "v2 decoder": int4 block-32;
-// soniqo MOSS guide RU, implementation notes: symmetric linear INT8 block-32).
+// soniqo MOSS guide RU, implementation notes: symmetric linear INT8 block-32);
+// int5 is the MLX default of the soniqo MOSS guide ("INT5 vs INT8"), for which
+// the pages give no rule, so the same one is read with Q = 15.
 // Scale rule and rounding (this library's reading of those pages):
-//   amax = max |w| over the 32 values;  s = binary16_rne(amax / Q), Q = 7 or 127,
-//   fp32 division;  s == 0 -> all codes 0;  else q = clamp(rne(w / s), lo, hi)
-//   with fp32 division by the stored binary16 scale.
+//   amax = max |w| over the 32 values;  s = binary16_rne(amax / Q), Q = 7, 15
+//   or 127, fp32 division;  s == 0 -> all codes 0;  else
+//   q = clamp(rne(w / s), -Q-1, Q) with fp32 division by the stored binary16 scale.
+// int5 row layout: K/2 bytes of the low 4 bits of every code (as int4), then
+// K/8 bytes of bit 4 of every code (code k in bit k%8 of byte k/8).
 // The library is built with correctly rounded fp32 division and without
 // denormal flushing, so the result is bit-exact.
 #include "wq_internal.h"
@@ -23,8 +27,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
                                                    int64_t K, uint8_t *__restrict__ q,
                                                    uint16_t *__restrict__ scales)
 {
-    constexpr float kQ = BITS == 4 ? 7.0f : 127.0f;
-    constexpr float kLo = BITS == 4 ? -8.0f : -128.0f;
+    constexpr float kQ = BITS == 4 ? 7.0f : BITS == 5 ? 15.0f : 127.0f;
+    constexpr float kLo = -kQ - 1.0f;
     constexpr float kHi = kQ;
     const int64_t nb = K / kBlock;
     const int64_t total = N * nb;
@@ -66,9 +70,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
         }
         scales[i] = sbits;
 
-        if (BITS == 4) {
+        if (BITS == 4 || BITS == 5) {
             // byte j holds code 2j (low nibble) and 2j+1 (high nibble); dword d
-            // holds codes 8d..8d+7 at nibble positions 0..7.
+            // holds codes 8d..8d+7 at nibble positions 0..7 (int5: their low
+            // 4 bits, and bit 4 of code j in bit j of the block's high-bit dword)
+            const int64_t row = BITS == 4 ? K / 2 : K / 2 + K / 8;
             u4 out;
             uint32_t dw[4];
 #pragma unroll
@@ -79,7 +85,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
                 dw[d] = acc;
             }
             out.x = dw[0]; out.y = dw[1]; out.z = dw[2]; out.w = dw[3];
-            *reinterpret_cast<u4 *>(q + n * (K / 2) + b * 16) = out;
+            *reinterpret_cast<u4 *>(q + n * row + b * 16) = out;
+            if (BITS == 5) {
+                uint32_t hb = 0;
+#pragma unroll
+                for (int j = 0; j < kBlock; ++j) hb |= (((uint32_t)code[j] >> 4) & 1u) << j;
+                *reinterpret_cast<uint32_t *>(q + n * row + K / 2 + b * 4) = hb;
+            }
         } else {
             uint32_t dw[8];
 #pragma unroll
@@ -111,7 +123,28 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__
         const int64_t n = i / nb;
         const int64_t b = i - n * nb;
         uint32_t out[8];
-        if (BITS == 4) {
+        if (BITS == 5) {
+            const int64_t row = K / 2 + K / 8;
+            const u4 in = *reinterpret_cast<const u4 *>(q + n * row + b * 16);
+            const uint32_t hb = *reinterpret_cast<const uint32_t *>(q + n * row + K / 2 + b * 4);
+            const uint32_t dw[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // 5-bit field: nibble e (and e+4) of dword d with its bit 4, sign-extended
+                    const uint32_t fa = ((dw[d] >> (4 * e)) & 0xFu) | (((hb >> (8 * d + e)) & 1u) << 4);
+                    const uint32_t fc = ((dw[d] >> (4 * e + 16)) & 0xFu) | (((hb >> (8 * d + e + 4)) & 1u) << 4);
+                    const int32_t a = (int32_t)(fa << 27) >> 27;
+                    const int32_t c = (int32_t)(fc << 27) >> 27;
+                    lo |= ((uint32_t)a & 0xFFu) << (8 * e);
+                    hi |= ((uint32_t)c & 0xFFu) << (8 * e);
+                }
+                out[2 * d] = lo;
+                out[2 * d + 1] = hi;
+            }
+        } else if (BITS == 4) {
             const u4 in = *reinterpret_cast<const u4 *>(q + n * (K / 2) + b * 16);
             const uint32_t dw[4] = {in.x, in.y, in.z, in.w};
 #pragma unroll
@@ -159,6 +192,8 @@ hipError_t launch_pack(const float *w, int64_t N, int64_t K, int bits, void *q,
     const unsigned grid = grid_for(N * (K / kBlock));
     if (bits == 4)
         pack_kernel<4><<<grid, 256, 0, stream>>>(w, N, K, (uint8_t *)q, scales);
+    else if (bits == 5)
+        pack_kernel<5><<<grid, 256, 0, stream>>>(w, N, K, (uint8_t *)q, scales);
     else
         pack_kernel<8><<<grid, 256, 0, stream>>>(w, N, K, (uint8_t *)q, scales);
     return hipGetLastError();
@@ -170,6 +205,8 @@ hipError_t launch_unpack(const void *q, int64_t N, int64_t K, int bits, int8_t *
     const unsigned grid = grid_for(N * (K / kBlock));
     if (bits == 4)
         unpack_kernel<4><<<grid, 256, 0, stream>>>((const uint8_t *)q, N, K, codes);
+    else if (bits == 5)
+        unpack_kernel<5><<<grid, 256, 0, stream>>>((const uint8_t *)q, N, K, codes);
     else
         unpack_kernel<8><<<grid, 256, 0, stream>>>((const uint8_t *)q, N, K, codes);
     return hipGetLastError();

@@ -146,7 +146,7 @@ def pack(w, bits: int, q=None, scales=None, check_range: bool = True, stream=Non
     _need(w.dim() == 2, "w must be [N, K]")
     N, K = w.shape
     if check_range and w.numel():
-        Qmax = 7 if bits == 4 else 127
+        Qmax = {4: 7, 5: 15}.get(bits, 127)
         _need(bool(torch.isfinite(w).all()), "w has non-finite values")
         _need(float(w.abs().max()) <= 65504.0 * Qmax, "a block scale would overflow binary16")
     if q is None:
