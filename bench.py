@@ -253,6 +253,45 @@ def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
     return out
 
 
+def int5_leg(torch, wqa, inputs, np, oracle, steps, warmup):
+    """INT5 (f4): the decode step with every projection packed in int5 (lm_head
+    int8) as one grouped launch, and the M=4096 gate projection in int5 through
+    the prefill GEMM."""
+    wl = inputs.decode_step(1, proj_bits=5)
+    pkgs, calls, ys, host_w, _ = build_decode(torch, wqa, wl, COPIES)
+    launch_ms, wall_ms = time_grouped(torch, calls, steps, warmup)
+    worst = check_outputs(wl, ys, host_w, np, oracle)
+    del pkgs, calls, ys
+    torch.cuda.empty_cache()
+    out = {"workload": wl.name,
+           "decode_grouped": {"ms_per_step": round(wall_ms, 5), "launch_ms": round(launch_ms, 5),
+                              "weight_bytes": wl.weight_bytes,
+                              "weight_gbs": round(wl.weight_bytes / (wall_ms * 1e-3) / 1e9, 1),
+                              "algorithmic_gbs": round(wl.total_bytes / (launch_ms * 1e-3) / 1e9, 1),
+                              "hbm_frac": round(wl.total_bytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "worst_err_over_bound": round(worst, 4)}}
+    lp = inputs.long_prefill()
+    t = lp.tensors[0]                                       # gate 1024 -> 3072 at M=4096
+    q, sc = wqa.pack(torch.from_numpy(lp.weight(t)).cuda(), 5)
+    x = torch.from_numpy(lp.x_for(t)).cuda()
+    y = torch.empty((t.M, t.N), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        wqa.linear(x, q, sc, 5, out=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    a.record()
+    for _ in range(reps):
+        wqa.linear(x, q, sc, 5, out=y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tf = 2 * t.M * t.N * t.K / (ms * 1e-3) / 1e12
+    out["gemm_gate_m4096"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                              "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def prefill_leg(torch, wqa, inputs, steps, warmup):
     """M=4096 gate/up/down (int4) + int8 lm_head on the last 64 rows, via wq_linear."""
     wl = inputs.long_prefill()
@@ -434,6 +473,8 @@ def main() -> int:
     }
     log("shared-input fusion (113 GEMVs)")
     result["decode_step_fused"] = fused_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
+    log("int5 decode step and GEMM")
+    result["int5"] = int5_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
     if not args.no_prefill:
         log("prefill leg")
         result["prefill"] = prefill_leg(torch, wqa, inputs, max(3, args.steps // 10), max(1, args.warmup // 10))

@@ -206,13 +206,15 @@ def single_gemv() -> Workload:
                     description="one int4 GEMV, M=1, 1024->2048", single_stream_seed=0)
 
 
-def decode_step(M: int = 1, mixed: bool = False, fused: bool = False) -> Workload:
+def decode_step(M: int = 1, mixed: bool = False, fused: bool = False, proj_bits: int = 4) -> Workload:
     """One decode step: 28 layers x 7 projections + the tied lm_head (int8).
 
     int4 everywhere but the lm_head; with ``mixed`` the attention projections
     (q, k, v, o) are int8 and the MLP (gate, up, down) int4. With ``fused`` the
     projections that share an input are stacked along N (q|k|v, gate|up): the
-    same weights and activations, 113 GEMVs instead of 197.
+    same weights and activations, 113 GEMVs instead of 197. ``proj_bits`` = 5
+    packs every projection in int5 (the MLX default of the soniqo guide), the
+    lm_head staying int8.
     """
     config = 3 if mixed else 1
     tensors: List[TensorSpec] = []
@@ -223,7 +225,7 @@ def decode_step(M: int = 1, mixed: bool = False, fused: bool = False) -> Workloa
         for name, parts in groups:
             K, group = proj[parts[0]]
             N = sum(PROJ_N[p] for p in parts)
-            bits = 8 if (mixed and group in ("attn", "o")) else 4
+            bits = 8 if (mixed and group in ("attn", "o")) else proj_bits
             key = f"L{layer}.{group}"
             if key not in acts:
                 acts[key] = _act(config, M, layer, group, K)
@@ -231,8 +233,8 @@ def decode_step(M: int = 1, mixed: bool = False, fused: bool = False) -> Workloa
                                       bits, act=key, M=M, parts=parts if len(parts) > 1 else ()))
     acts["lm"] = _act(config, M, 0, "lm", HIDDEN)
     tensors.append(TensorSpec("lm_head", 0, "lm_head", HIDDEN, VOCAB, 8, act="lm", M=M))
-    kind = "mixed int8-attn/int4-mlp" if mixed else "int4"
-    return Workload(f"decode_step_{'mixed' if mixed else 'int4'}_m{M}{'_fused' if fused else ''}", config, M,
+    kind = "mixed int8-attn/int4-mlp" if mixed else f"int{proj_bits}"
+    return Workload(f"decode_step_{'mixed' if mixed else kind}_m{M}{'_fused' if fused else ''}", config, M,
                     tensors, acts,
                     description=f"one decode step, M={M}, {kind}, {len(tensors)} GEMVs incl. int8 lm_head"
                                 + (", q|k|v and gate|up stacked along N" if fused else ""))
