@@ -1,4 +1,4 @@
-// wq_gemv.hip -- decode GEMV for block-32 int4 / int8 weights, 1 <= M <= 16.
+// wq_gemv.hip -- decode GEMV for block-32 int4 / int5 / int8 weights, 1 <= M <= 16.
 //
 // The devpost page for TinyMOSS-Diarize ("How we built it") describes a
 // separate GEMV path for decode that multiplies straight out of the packed
@@ -23,6 +23,8 @@
 //    flight across it, and the arithmetic starts on each chunk as it lands. x
 //    is stored unpadded with an XOR swizzle of its 16-byte pieces so that the
 //    128-bit reads of 16 lanes hit distinct banks.
+//  * int5 rows are read as int4 chunks of low nibbles plus, per chunk, the 4
+//    bytes of its codes' bit 4 (a second load from the row's bit-4 plane).
 //  * Unpack in registers without int->float conversions (wq_decode.h); the fp32
 //    FMA takes the binary16 code directly as an operand (v_fma_mix_f32), so each
 //    product q*x is exact and is accumulated in fp32.
@@ -297,6 +299,9 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
     const uint32_t qrow = (uint32_t)K * BITS / 8;     // bytes per row of codes
     const int nseg = CPL / S;
     const DecodeConsts dc = DecodeConsts::make();
+    Decode5Consts dc5;
+    if constexpr (BITS == 5) dc5 = Decode5Consts::make();
+    constexpr int NL = BITS == 5 ? 2 * J * S : J * S;   // loads per segment (int5: + bit-4 dwords)
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * qrow);   // N * qrow < 2^32 (host check)
     uint8_t *xs = lds;                                                      // [MT][NB][8] pieces
     uint16_t *ss = reinterpret_cast<uint16_t *>(lds + MT * NB * 128);       // [IROWS][NB]
@@ -309,6 +314,7 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
     }
 
     u4 w[J][S];
+    uint32_t hw[J][S];                          // int5: the chunks' bit-4 dwords
     const int mend = MLOOP ? M : 1;            // without MLOOP, M <= MT: one pass
     for (int mg = 0; mg < mend; mg += MT) {
         float acc[J][MT];
@@ -339,7 +345,15 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
                         w[j][c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
                                                              qr, rowq[j] + (uint32_t)((seg * S + c) * G + li) * 16,
                                                              0, kNonTemporal));
-                copies_barrier<J * S>();                                 // codes stay in flight
+                if constexpr (BITS == 5) {
+#pragma unroll
+                    for (int c = 0; c < S; ++c)
+#pragma unroll
+                        for (int j = 0; j < J; ++j)
+                            hw[j][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                                qr, rowq[j] + (uint32_t)K / 2 + (uint32_t)((seg * S + c) * G + li) * 4, 0, kNonTemporal);
+                }
+                copies_barrier<NL>();                                    // codes stay in flight
             } else {
                 copies_barrier<0>();
             }
@@ -354,18 +368,21 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
 #pragma unroll
             for (int c = 0; c < S; ++c) {
                 const int blk = c * G / CPB + blk0;                      // block within the segment
-                const int cofs = (BITS == 4 ? c : (c & ~1)) * (G / CPB) * 128;
+                const int cofs = (BITS != 8 ? c : (c & ~1)) * (G / CPB) * 128;
                 const uint8_t *xp[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) xp[k] = ((BITS == 8 && (c & 1)) ? xpo[k] : xpe[k]) + cofs;
                 float sc[J];
                 u4 wc[J];
+                uint32_t hc[J];
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
                     sc[j] = (float)__builtin_bit_cast(_Float16, ss[(lrow0 + j) * NB + blk]);
                     wc[j] = w[j][c];
+                    hc[j] = hw[j][c];
                 }
-                chunk_fma<BITS, MT, J>(wc, xp, NB * 128, dc, sc, acc);
+                if constexpr (BITS == 5) chunk_fma5<MT, J>(wc, hc, xp, NB * 128, dc5, sc, acc);
+                else chunk_fma<BITS, MT, J>(wc, xp, NB * 128, dc, sc, acc);
                 __builtin_amdgcn_sched_barrier(0);   // keep each chunk's work together (bounds live registers)
             }
         }
@@ -457,8 +474,17 @@ __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint
     const int K = (int)d.K;
     const GemvGeom g = gemv_geom(K, BITS, d.N, true);
     const int64_t row0 = item * g.rows;
-    if constexpr (BITS == 5) {
-        gemv_item_general<5, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
+    // int5 with 4 activation rows in registers (3 or 4 rows, one pass): the fast
+    // forms' chunks plus their bit-4 dwords would not fit the grouped kernel's
+    // register bound, so these items take the general form (one row per lane,
+    // the same arithmetic and results), twice when the item holds two rows per
+    // lane.
+    if constexpr (BITS == 5 && MT == 4 && !MLOOP) {
+        const int64_t half = (int64_t)kGemvWaves * (kWave / g.G);
+        for (int64_t r = 0; r < g.rows; r += half) {
+            if (r > 0) copies_barrier<0>();       // the first pass's LDS readers are done
+            gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0 + r, g, lds);
+        }
     } else {
         switch (g.kind) {
         case kGemvJ2S2: gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
@@ -466,7 +492,7 @@ __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint
         case kGemvJ1S4: gemv_item_fast<BITS, MT, 1, 4, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
         case kGemvJ1S6:
         case kGemvJ1S8:
-            gemv_item_fast<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+            gemv_item_fast<BITS, MT, 1, BITS == 8 ? 8 : 6, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
             break;
         default: gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds); break;
         }
@@ -513,15 +539,13 @@ hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const
                           const uint16_t *s, float *y, hipStream_t stream)
 {
     const GemvGeom g = gemv_geom(K, BITS, N, false);
-    if constexpr (BITS == 5) {
-        return launch_kind<5, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
-    } else {
+    {
         switch (g.kind) {
         case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
         case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
         case kGemvJ1S4: return launch_kind<BITS, MT, 1, 4, MLOOP>(x, M, K, N, q, s, y, g, stream);
         case kGemvJ1S6:
-        case kGemvJ1S8: return launch_kind<BITS, MT, 1, BITS == 4 ? 6 : 8, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        case kGemvJ1S8: return launch_kind<BITS, MT, 1, BITS == 8 ? 8 : 6, MLOOP>(x, M, K, N, q, s, y, g, stream);
         default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
         }
     }

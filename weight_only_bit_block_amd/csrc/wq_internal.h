@@ -22,7 +22,7 @@ constexpr int kWave = 64;           // gfx950 wavefront size
 // workgroup item is IROWS = 4 * (64/G) * J consecutive rows of one tensor.
 //
 // int5 rows (the low-nibble plane, then the bit-4 plane) are read as int4
-// chunks plus the chunk's 4 bytes of bit 4, in the general form.
+// chunks plus each chunk's 4 bytes of bit 4, in either form.
 //
 // Fast form (G == 16 and K % 256 == 0: every shape of the decoder): a lane owns
 // J rows and holds S of its chunks per row in registers at a time; the row is
@@ -61,14 +61,14 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
     g.J = 1;
     g.S = 1;
     g.kind = kGemvGeneral;
-    if (G == 16 && K % 256 == 0 && bits != 5) {
+    if (G == 16 && K % 256 == 0) {
         const int64_t rows_j2 = (int64_t)kGemvWaves * 4 * 2;
         if (g.CPL == 2) {
             const bool few = !grouped && (N + rows_j2 - 1) / rows_j2 < 256;
             g.kind = few ? kGemvJ1S2 : kGemvJ2S2;
             g.J = few ? 1 : 2;
             g.S = 2;
-        } else if (bits == 4 && g.CPL % 6 == 0) {
+        } else if (bits != 8 && g.CPL % 6 == 0) {
             g.kind = kGemvJ1S6; g.S = 6;
         } else if (bits == 8 && g.CPL % 8 == 0) {
             g.kind = kGemvJ1S8; g.S = 8;
