@@ -92,10 +92,15 @@ int wq_unpack(const void *q, int64_t N, int64_t K, int bits,
 
 /*
  * wq_gemv -- decode path (the devpost page's separate GEMV path for decode),
- * 1 <= M <= 16. Codes are unpacked in registers and multiplied in fp32 with
- * fused multiply-adds against the fp32 activations; each block's partial is
- * scaled by its fp32-converted scale; lanes along K are reduced within a
- * wavefront. Error: |y - y_exact| <= 1e-5 * sum_k |x[m,k]| |w^[n,k]|.
+ * 1 <= M <= 16. M <= 2: codes are unpacked in registers and multiplied in fp32
+ * with fused multiply-adds against the fp32 activations; each block's partial
+ * is scaled by its fp32-converted scale; lanes along K are reduced within a
+ * wavefront. 3 <= M <= 16: x is split exactly into three binary16 parts per
+ * (row, block) after a power-of-two normalisation, and the block partials come
+ * from fp16 matrix-core instructions with exact products and fp32 sums, then
+ * are scaled per block in fp32 as above.
+ * Error: |y - y_exact| <= 1e-5 * sum_k |x[m,k]| |w^[n,k]| (M >= 3: for x blocks
+ * whose largest magnitude is at least 2^-112).
  */
 int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
             const void *q, const uint16_t *scales, float *y, hipStream_t stream);

@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libwq.so")
 OBJDIR = os.path.join(ROOT, "_build", "wq")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["wq_abi.cpp", "wq_pack.hip", "wq_gemv.hip", "wq_gemm.hip", "wq_embed.hip"]
+SOURCES = ["wq_abi.cpp", "wq_pack.hip", "wq_gemv.hip", "wq_mgemv.hip", "wq_gemm.hip", "wq_embed.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -121,6 +121,7 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     if (empty) return WQ_OK;
     st = gemv_offsets_ok(K, N, bits);
     if (st) return st;
+    if (M >= wq::kMgemvMinM) return hip_status(wq::launch_mgemv(x, M, K, N, bits, q, scales, y, stream));
     return hip_status(wq::launch_gemv(x, M, K, N, bits, q, scales, y, stream));
 }
 
@@ -215,7 +216,7 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
             if (!aligned(d.x, 16) || !aligned(d.y, 16)) return WQ_ERR_ALIGN;
         }
         d.tile_begin = cur;
-        const int64_t rows = wq::gemv_geom(d.K, d.bits, d.N, true).rows;
+        const int64_t rows = wq::decode_item_rows(d.K, d.bits, d.N, true, M);
         cur += (d.N + rows - 1) / rows;
         if (cur > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
     }
@@ -231,6 +232,7 @@ int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count, int64
     if (count == 0 || total_tiles == 0) return WQ_OK;
     if (!base || !table_dev) return WQ_ERR_NULL;
     if (!aligned(base, WQ_TABLE_ALIGN) || !aligned(table_dev, WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
+    if (M >= wq::kMgemvMinM) return hip_status(wq::launch_mgemv_grouped(base, table_dev, count, total_tiles, M, stream));
     return hip_status(wq::launch_gemv_grouped(base, table_dev, count, total_tiles, M, stream));
 }
 

@@ -51,6 +51,18 @@ __device__ __forceinline__ float fmix(_Float16 w, float x, float acc)
     return __builtin_fmaf((float)w, x, acc);   // one v_fma_mix_f32: exact product, one rounding
 }
 
+// A code as fp32 (exact). With one activation row the conversion folds into
+// v_fma_mix_f32; with several, each code is converted once and the MT products
+// use the full-rate v_fma_f32 (v_fma_mix_f32 issues at half rate on gfx950).
+// The arithmetic is the same either way: exact product, one rounding.
+template <int MT>
+__device__ __forceinline__ float code_f32(_Float16 w)
+{
+    float f = (float)w;
+    if constexpr (MT > 1) asm volatile("" : "+v"(f));
+    return f;
+}
+
 // y pointers come from kernel arguments or the tensor table; both are global
 // memory, so store through the global address space.
 __device__ __forceinline__ void store_global(float *p, float v)
@@ -166,30 +178,46 @@ __device__ __forceinline__ void chunk_fma(const u4 (&w)[J], const uint8_t *const
             h2 t0, t1, t2, t3;
             if (BITS == 4) {
                 decode_int4(w[j][h], dc, t0, t1, t2, t3);     // (k0,k4) (k1,k5) (k2,k6) (k3,k7)
+                const float ft0x = code_f32<MT>(t0.x);
+                const float ft0y = code_f32<MT>(t0.y);
+                const float ft1x = code_f32<MT>(t1.x);
+                const float ft1y = code_f32<MT>(t1.y);
+                const float ft2x = code_f32<MT>(t2.x);
+                const float ft2y = code_f32<MT>(t2.y);
+                const float ft3x = code_f32<MT>(t3.x);
+                const float ft3y = code_f32<MT>(t3.y);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    p0[j][m] = fmix(t0.x, xa[m].x, p0[j][m]);
-                    p1[j][m] = fmix(t0.y, xb[m].x, p1[j][m]);
-                    p0[j][m] = fmix(t1.x, xa[m].y, p0[j][m]);
-                    p1[j][m] = fmix(t1.y, xb[m].y, p1[j][m]);
-                    p0[j][m] = fmix(t2.x, xa[m].z, p0[j][m]);
-                    p1[j][m] = fmix(t2.y, xb[m].z, p1[j][m]);
-                    p0[j][m] = fmix(t3.x, xa[m].w, p0[j][m]);
-                    p1[j][m] = fmix(t3.y, xb[m].w, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft0x, xa[m].x, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft0y, xb[m].x, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft1x, xa[m].y, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft1y, xb[m].y, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft2x, xa[m].z, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft2y, xb[m].z, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft3x, xa[m].w, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft3y, xb[m].w, p1[j][m]);
                 }
             } else {
                 decode_int8(w[j][2 * h], dc, t0, t1);         // (k0,k2) (k1,k3)
                 decode_int8(w[j][2 * h + 1], dc, t2, t3);     // (k4,k6) (k5,k7)
+                const float ft0x = code_f32<MT>(t0.x);
+                const float ft0y = code_f32<MT>(t0.y);
+                const float ft1x = code_f32<MT>(t1.x);
+                const float ft1y = code_f32<MT>(t1.y);
+                const float ft2x = code_f32<MT>(t2.x);
+                const float ft2y = code_f32<MT>(t2.y);
+                const float ft3x = code_f32<MT>(t3.x);
+                const float ft3y = code_f32<MT>(t3.y);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    p0[j][m] = fmix(t0.x, xa[m].x, p0[j][m]);
-                    p1[j][m] = fmix(t0.y, xa[m].z, p1[j][m]);
-                    p0[j][m] = fmix(t1.x, xa[m].y, p0[j][m]);
-                    p1[j][m] = fmix(t1.y, xa[m].w, p1[j][m]);
-                    p0[j][m] = fmix(t2.x, xb[m].x, p0[j][m]);
-                    p1[j][m] = fmix(t2.y, xb[m].z, p1[j][m]);
-                    p0[j][m] = fmix(t3.x, xb[m].y, p0[j][m]);
-                    p1[j][m] = fmix(t3.y, xb[m].w, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft0x, xa[m].x, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft0y, xa[m].z, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft1x, xa[m].y, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft1y, xa[m].w, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft2x, xb[m].x, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft2y, xb[m].z, p1[j][m]);
+                    p0[j][m] = __builtin_fmaf(ft3x, xb[m].y, p0[j][m]);
+                    p1[j][m] = __builtin_fmaf(ft3y, xb[m].w, p1[j][m]);
                 }
             }
         }
@@ -224,16 +252,24 @@ __device__ __forceinline__ void chunk_fma5(const u4 (&w)[J], const uint32_t (&hb
         for (int j = 0; j < J; ++j) {
             h2 t0, t1, t2, t3;
             decode_int5(w[j][h], hb[j] >> (8 * h), dc, t0, t1, t2, t3);   // (k0,k4) (k1,k5) (k2,k6) (k3,k7)
+            const float ft0x = code_f32<MT>(t0.x);
+            const float ft0y = code_f32<MT>(t0.y);
+            const float ft1x = code_f32<MT>(t1.x);
+            const float ft1y = code_f32<MT>(t1.y);
+            const float ft2x = code_f32<MT>(t2.x);
+            const float ft2y = code_f32<MT>(t2.y);
+            const float ft3x = code_f32<MT>(t3.x);
+            const float ft3y = code_f32<MT>(t3.y);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                p0[j][m] = fmix(t0.x, xa[m].x, p0[j][m]);
-                p1[j][m] = fmix(t0.y, xb[m].x, p1[j][m]);
-                p0[j][m] = fmix(t1.x, xa[m].y, p0[j][m]);
-                p1[j][m] = fmix(t1.y, xb[m].y, p1[j][m]);
-                p0[j][m] = fmix(t2.x, xa[m].z, p0[j][m]);
-                p1[j][m] = fmix(t2.y, xb[m].z, p1[j][m]);
-                p0[j][m] = fmix(t3.x, xa[m].w, p0[j][m]);
-                p1[j][m] = fmix(t3.y, xb[m].w, p1[j][m]);
+                p0[j][m] = __builtin_fmaf(ft0x, xa[m].x, p0[j][m]);
+                p1[j][m] = __builtin_fmaf(ft0y, xb[m].x, p1[j][m]);
+                p0[j][m] = __builtin_fmaf(ft1x, xa[m].y, p0[j][m]);
+                p1[j][m] = __builtin_fmaf(ft1y, xb[m].y, p1[j][m]);
+                p0[j][m] = __builtin_fmaf(ft2x, xa[m].z, p0[j][m]);
+                p1[j][m] = __builtin_fmaf(ft2y, xb[m].z, p1[j][m]);
+                p0[j][m] = __builtin_fmaf(ft3x, xa[m].w, p0[j][m]);
+                p1[j][m] = __builtin_fmaf(ft3y, xb[m].w, p1[j][m]);
             }
         }
     }

@@ -87,6 +87,18 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
     return g;
 }
 
+// Decode with 3..16 activation rows runs on the matrix cores (wq_mgemv.hip),
+// where the fp32-FMA form is bound by its LDS reads of x: a work item is 128
+// consecutive weight rows of one tensor.
+constexpr int kMgemvRows = 128;
+constexpr int kMgemvMinM = 3;
+
+// Rows per work item of a decode call with M activation rows.
+__host__ __device__ inline int64_t decode_item_rows(int64_t K, int bits, int64_t N, bool grouped, int64_t M)
+{
+    return M >= kMgemvMinM ? (int64_t)kMgemvRows : gemv_geom(K, bits, N, grouped).rows;
+}
+
 // Activation rows staged at once (m-group size): 1, 2 or 4.
 __host__ __device__ inline int gemv_mt(int64_t M) { return M <= 2 ? (int)M : kGemvMaxMT; }
 
@@ -127,6 +139,10 @@ hipError_t launch_gemv_grouped(const void *base, const wq_desc *table_dev, int c
                                int64_t total_tiles, int64_t M, hipStream_t stream);
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
                        const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+hipError_t launch_mgemv(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
+                        const uint16_t *scales, float *y, hipStream_t stream);
+hipError_t launch_mgemv_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_items,
+                                int64_t M, hipStream_t stream);
 hipError_t launch_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits,
                         const void *q, const uint16_t *scales, float *out, hipStream_t stream);
 
