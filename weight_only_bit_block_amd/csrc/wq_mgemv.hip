@@ -49,15 +49,20 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSB = 8;                           // blocks per segment
-constexpr int kRowBytes = kSB * 32 * 2;          // one operand row of a segment, binary16
-constexpr int kOpBytes = 32 * kRowBytes;         // one 32-row operand (8 activation rows, 3 parts)
-constexpr int kEBytes = 16 * kSB * 4;            // 2^-e per (block, x row): [kSB][16] floats
+// Blocks per segment: 8, or 4 for int8 codes and for M > 8, so that the
+// workgroup's LDS (two operand buffers and two code buffers) stays near 72 KiB
+// and two workgroups share a compute unit.
+template <int BITS, int MF>
+constexpr int seg_blocks() { return (MF == 1 && BITS != 8) ? 8 : 4; }
 
-template <int MF>
+// Operand buffer of a segment of SB blocks: MF 32-row operands (binary16, row
+// pitch SB * 64 bytes) and the factors 2^-e, [SB][16] floats.
+template <int MF, int SB>
 struct Buf {
-    static constexpr int A_BYTES = MF * kOpBytes;
-    static constexpr int BYTES = A_BYTES + kEBytes;
+    static constexpr int ROW_BYTES = SB * 32 * 2;
+    static constexpr int OP_BYTES = 32 * ROW_BYTES;
+    static constexpr int A_BYTES = MF * OP_BYTES;
+    static constexpr int BYTES = A_BYTES + 16 * SB * 4;
 };
 
 template <int CTRL>
@@ -66,70 +71,131 @@ __device__ __forceinline__ float dpp(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// 16-byte slot s of operand row r (32 slots per row in a segment)
-__device__ __forceinline__ int aoff(int r, int s) { return r * kRowBytes + ((s ^ r) & 31) * 16; }
+// 16-byte slot s of operand row r (4 * SB slots per row of a segment)
+template <int SB>
+__device__ __forceinline__ int aoff(int r, int s) { return r * (SB * 64) + ((s ^ r) & (4 * SB - 1)) * 16; }
 
-// Lane (n, g) codes of one block as two groups of 8 in unpack order, (int5) the
-// two bytes of their bit 4, and the block's scale.
-template <int BITS>
-struct LaneCodes {
-    uint32_t v[BITS == 8 ? 4 : 2];
-    uint32_t h;
-    uint32_t sc;
+// A wavefront's codes of one segment in LDS, copied there directly (no
+// registers). Row rr of its 32 weight rows holds the segment's SB blocks in
+// 16-byte pieces; piece p is stored at slot p ^ swz(rr) so that the matrix
+// operand reads of 32 rows spread over the banks. int5 adds the rows' bit-4
+// dwords, [32 rows][SB dwords].
+template <int BITS, int SB>
+struct BStage {
+    static constexpr int SLOTS = SB * (BITS == 8 ? 2 : 1);       // 16-byte pieces per row
+    static constexpr int ROW = SLOTS * 16;
+    static constexpr int CODE_BYTES = 32 * ROW;
+    static constexpr int H_BYTES = BITS == 5 ? 32 * SB * 4 : 0;
+    static constexpr int WAVE_BYTES = CODE_BYTES + H_BYTES;
+    static constexpr int BYTES = 4 * WAVE_BYTES;                  // the workgroup's 4 wavefronts
+    // the rows read together by one LDS read hit distinct banks
+    __device__ static constexpr int swz(int rr) { return (rr / (16 / SLOTS)) % SLOTS; }
 };
 
-template <int BITS>
-__device__ __forceinline__ LaneCodes<BITS> load_codes(__amdgpu_buffer_rsrc_t qr, __amdgpu_buffer_rsrc_t sr,
-                                                      uint32_t rowq, uint32_t hrow, uint32_t rows, int b, int g)
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_base, uint32_t off)
 {
-    LaneCodes<BITS> c;
-    c.sc = __builtin_amdgcn_raw_buffer_load_b16(sr, rows + (uint32_t)b * 2, 0, 0);
-    if constexpr (BITS == 8) {
-        const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(qr, rowq + (uint32_t)b * 32 + g * 16, 0, 0));
-        c.v[0] = v.x; c.v[1] = v.y; c.v[2] = v.z; c.v[3] = v.w;
-        c.h = 0;
-    } else {
-        const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(qr, rowq + (uint32_t)b * 16 + g * 8, 0, 0));
-        c.v[0] = v.x; c.v[1] = v.y;
-        c.h = 0;
-        if constexpr (BITS == 5)
-            c.h = __builtin_amdgcn_raw_buffer_load_b16(qr, hrow + (uint32_t)b * 4 + g * 2, 0, 0);
-    }
-    return c;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, off, 0, 0, 0);
 }
 
-template <int BITS>
-__device__ __forceinline__ void unpack_codes(const LaneCodes<BITS> &c, const DecodeConsts &dc,
-                                             const Decode5Consts &dc5, h8 (&b)[2])
+// Issue the copies of segment b0 .. b0+SB-1 of weight rows nrow0 .. nrow0+31
+// into this wavefront's region dst: each instruction moves 64 / SLOTS whole rows
+// (full cache lines). Reads past the tensor return zeros; blocks past K read
+// the next row's codes, whose scale is taken as 0.
+template <int BITS, int SB>
+__device__ __forceinline__ void stage_codes(__amdgpu_buffer_rsrc_t qr, uint32_t qrow, int K, int64_t nrow0, int64_t N,
+                                            int b0, uint8_t *dst, int lane)
 {
-    if constexpr (BITS == 4) {
-        b[0] = unpack8_int4(c.v[0], dc);
-        b[1] = unpack8_int4(c.v[1], dc);
-    } else if constexpr (BITS == 5) {
-        b[0] = unpack8_int5(c.v[0], c.h & 0xFF, dc5);
-        b[1] = unpack8_int5(c.v[1], c.h >> 8, dc5);
-    } else {
-        b[0] = unpack8_int8(c.v[0], c.v[1], dc);
-        b[1] = unpack8_int8(c.v[2], c.v[3], dc);
+    using B = BStage<BITS, SB>;
+    constexpr int RPI = 64 / B::SLOTS;             // rows per instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int rr = i * RPI + lane / B::SLOTS;
+        const int p = (lane % B::SLOTS) ^ B::swz(rr);
+        int64_t n = nrow0 + rr;
+        n = n < N ? n : N - 1;
+        copy16(qr, dst + i * 1024, (uint32_t)n * qrow + (uint32_t)b0 * (B::ROW / SB) + (uint32_t)p * 16);
     }
+    if constexpr (BITS == 5) {
+        // the rows' bit-4 dwords: SB / 4 pieces of 16 bytes per row
+        constexpr int PR = SB / 4;
+        const int rr = lane / PR, h = lane % PR;    // dwords 4h .. 4h+3 of row rr
+        if (rr < 32) {
+            int64_t n = nrow0 + rr;
+            n = n < N ? n : N - 1;
+            copy16(qr, dst + B::CODE_BYTES, (uint32_t)n * qrow + (uint32_t)K / 2 + (uint32_t)(b0 + 4 * h) * 4);
+        }
+    }
+}
+
+// Lane (r, g): codes 16g .. 16g+15 of block j of its row, as two groups of 8 in
+// unpack order.
+template <int BITS, int SB>
+__device__ __forceinline__ void lane_codes(const uint8_t *src, int r, int g, int j, const DecodeConsts &dc,
+                                           const Decode5Consts &dc5, h8 (&b)[2])
+{
+    using B = BStage<BITS, SB>;
+    if constexpr (BITS == 8) {
+        const u4 v = *reinterpret_cast<const u4 *>(src + r * B::ROW + ((2 * j + g) ^ B::swz(r)) * 16);
+        b[0] = unpack8_int8(v.x, v.y, dc);
+        b[1] = unpack8_int8(v.z, v.w, dc);
+    } else {
+        const u2 v = *reinterpret_cast<const u2 *>(src + r * B::ROW + (j ^ B::swz(r)) * 16 + g * 8);
+        if constexpr (BITS == 4) {
+            b[0] = unpack8_int4(v.x, dc);
+            b[1] = unpack8_int4(v.y, dc);
+        } else {
+            const uint32_t h = *reinterpret_cast<const uint16_t *>(src + B::CODE_BYTES + r * (SB * 4) + j * 4 + g * 2);
+            b[0] = unpack8_int5(v.x, h & 0xFF, dc5);
+            b[1] = unpack8_int5(v.y, h >> 8, dc5);
+        }
+    }
+}
+
+// The scales of a segment for one row: SB binary16 values, packed two per
+// dword (one load when the row's scales are aligned for it).
+template <int SB>
+struct Scales {
+    uint32_t w[SB / 2];
+};
+
+template <int SB>
+__device__ __forceinline__ Scales<SB> load_scales(__amdgpu_buffer_rsrc_t sr, uint32_t rows, int C, int b0)
+{
+    Scales<SB> r;
+    if ((C & (SB - 1)) == 0) {
+        if constexpr (SB == 8) {
+            const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(sr, rows + (uint32_t)b0 * 2, 0, 0));
+            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+        } else {
+            const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(sr, rows + (uint32_t)b0 * 2, 0, 0));
+            r.w[0] = v.x; r.w[1] = v.y;
+        }
+        return r;
+    }
+#pragma unroll
+    for (int j = 0; j < SB / 2; ++j)
+        r.w[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, rows + (uint32_t)(b0 + 2 * j) * 2, 0, 0) |
+                 (__builtin_amdgcn_raw_buffer_load_b16(sr, rows + (uint32_t)(b0 + 2 * j + 1) * 2, 0, 0) << 16);
+    return r;
 }
 
 // x of one segment: group i (8 values) of the segment is row m, block blk,
-// k-group q (i = (m * kSB + blk) * 4 + q); a thread holds XG groups.
-constexpr int kXG = 16 * kSB * 4 / 256;          // groups per thread (M <= 16): 2
-
+// k-group q (i = (m * SB + blk) * 4 + q); a thread holds XG groups (16 rows).
+template <int SB>
 struct XStage {
-    f4 v[kXG][2];
+    static constexpr int XG = 16 * SB * 4 / 256;
+    f4 v[XG][2];
 };
 
-__device__ __forceinline__ void load_x(XStage &xs, const float *__restrict__ x, int M, int K, int b0, int t)
+template <int SB>
+__device__ __forceinline__ void load_x(XStage<SB> &xs, const float *__restrict__ x, int M, int K, int b0, int t)
 {
     const int C = K >> 5;
 #pragma unroll
-    for (int i = 0; i < kXG; ++i) {
+    for (int i = 0; i < XStage<SB>::XG; ++i) {
         const int idx = t + i * 256;
-        int m = idx / (kSB * 4);
-        const int blk = (idx / 4) % kSB, q = idx & 3;
+        int m = idx / (SB * 4);
+        const int blk = (idx / 4) % SB, q = idx & 3;
         int b = b0 + blk;
         m = m < M ? m : M - 1;                   // rows past M and blocks past K load valid data, unused
         b = b < C ? b : C - 1;
@@ -140,15 +206,16 @@ __device__ __forceinline__ void load_x(XStage &xs, const float *__restrict__ x, 
 }
 
 // Split the staged x into the operand rows and the per-(row, block) factors.
-template <int BITS, int MF>
-__device__ __forceinline__ void store_x(const XStage &xs, int M, uint8_t *buf, int t)
+template <int BITS, int MF, int SB>
+__device__ __forceinline__ void store_x(const XStage<SB> &xs, int M, uint8_t *buf, int t)
 {
-    float *E = reinterpret_cast<float *>(buf + Buf<MF>::A_BYTES);
+    using A = Buf<MF, SB>;
+    float *E = reinterpret_cast<float *>(buf + A::A_BYTES);
 #pragma unroll
-    for (int i = 0; i < kXG; ++i) {
+    for (int i = 0; i < XStage<SB>::XG; ++i) {
         const int idx = t + i * 256;
-        const int m = idx / (kSB * 4);
-        const int blk = (idx / 4) % kSB, q = idx & 3;
+        const int m = idx / (SB * 4);
+        const int blk = (idx / 4) % SB, q = idx & 3;
         const float v[8] = {xs.v[i][0].x, xs.v[i][0].y, xs.v[i][0].z, xs.v[i][0].w,
                             xs.v[i][1].x, xs.v[i][1].y, xs.v[i][1].z, xs.v[i][1].w};
         float mx = 0.0f;
@@ -177,39 +244,47 @@ __device__ __forceinline__ void store_x(const XStage &xs, int M, uint8_t *buf, i
         }
         if (m < M) {
             const int s = blk * 4 + q;
-            uint8_t *op = buf + (m >> 3) * kOpBytes;
+            uint8_t *op = buf + (m >> 3) * A::OP_BYTES;
             const int mm = m & 7;
-            *reinterpret_cast<h8 *>(op + aoff(mm, s)) = p1;
-            *reinterpret_cast<h8 *>(op + aoff(8 + mm, s)) = p2;
-            *reinterpret_cast<h8 *>(op + aoff(16 + mm, s)) = p3;
+            *reinterpret_cast<h8 *>(op + aoff<SB>(mm, s)) = p1;
+            *reinterpret_cast<h8 *>(op + aoff<SB>(8 + mm, s)) = p2;
+            *reinterpret_cast<h8 *>(op + aoff<SB>(16 + mm, s)) = p3;
             if (q == 0) E[blk * 16 + m] = __builtin_ldexpf(1.0f, -e);
         }
     }
 }
 
 // One item: weight rows row0 .. row0+127 of one tensor, all M activation rows
-// (M <= 8 * MF).
+// (M <= 8 * MF). bq0 / bq1: the two LDS buffers of the codes (separate arrays,
+// so reading one never waits for copies into the other).
 template <int BITS, int MF>
 __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, int K, int64_t N,
                                            const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
-                                           float *__restrict__ y, int64_t row0, uint8_t *__restrict__ lds)
+                                           float *__restrict__ y, int64_t row0, uint8_t *__restrict__ lds,
+                                           uint8_t *__restrict__ bq0, uint8_t *__restrict__ bq1)
 {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int r = lane & 31, g = lane >> 5;
+    constexpr int SB = seg_blocks<BITS, MF>();
+    using A = Buf<MF, SB>;
+    using BS = BStage<BITS, SB>;
     const int C = K >> 5;
-    const int nseg = (C + kSB - 1) / kSB;
+    const int nseg = (C + SB - 1) / SB;
     const uint32_t qrow = (uint32_t)K * BITS / 8;
     const DecodeConsts dc = DecodeConsts::make();
     Decode5Consts dc5;
     if constexpr (BITS == 5) dc5 = Decode5Consts::make();
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * qrow);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint64_t)N * C * 2);
-    int64_t n = row0 + wave * 32 + r;
+    const int64_t nrow0 = row0 + wave * 32;
+    int64_t n = nrow0 + r;
     const bool nvalid = n < N;
     n = nvalid ? n : N - 1;                      // rows past N reload the last row, not stored
-    const uint32_t rowq = (uint32_t)n * qrow, hrow = rowq + (uint32_t)K / 2, rows = (uint32_t)n * C * 2;
+    const uint32_t rows = (uint32_t)n * C * 2;
+    uint8_t *const w0 = bq0 + wave * BS::WAVE_BYTES;
+    uint8_t *const w1 = bq1 + wave * BS::WAVE_BYTES;
 
     float acc[MF][4];
 #pragma unroll
@@ -218,40 +293,48 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
         for (int v = 0; v < 4; ++v) acc[f][v] = 0.0f;
     const f16v zero = {};
 
-    LaneCodes<BITS> cd[kSB];
-    XStage xs;
-    // prologue: segment 0's x split into buffer 0, its codes in flight
-    load_x(xs, x, M, K, 0, t);
-#pragma unroll
-    for (int j = 0; j < kSB; ++j) cd[j] = load_codes<BITS>(qr, sr, rowq, hrow, rows, j < C ? j : C - 1, g);
-    store_x<BITS, MF>(xs, M, lds, t);
-    __syncthreads();
+    XStage<SB> xs;
+    Scales<SB> scv = load_scales<SB>(sr, rows, C, 0), scn = scv;
+    // prologue: segment 0's codes copied, its x split into buffer 0
+    stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, 0, w0, lane);
+    load_x<SB>(xs, x, M, K, 0, t);
+    store_x<BITS, MF, SB>(xs, M, lds, t);
+    lds_barrier();
 
-    for (int seg = 0; seg < nseg; ++seg) {
-        const int b0 = seg * kSB;
-        const uint8_t *buf = lds + (seg & 1) * Buf<MF>::BYTES;
-        const float *E = reinterpret_cast<const float *>(buf + Buf<MF>::A_BYTES);
-        if (seg + 1 < nseg) load_x(xs, x, M, K, b0 + kSB, t);
+    // One segment: codes from bcur; the next segment's codes into bnext and its
+    // x into the other operand buffer.
+    auto segment = [&](int seg, const uint8_t *bcur, uint8_t *bnext) {
+        const int b0 = seg * SB;
+        const uint8_t *buf = lds + (seg & 1) * A::BYTES;
+        const float *E = reinterpret_cast<const float *>(buf + A::A_BYTES);
+        const bool more = seg + 1 < nseg;
+        // Everything this wavefront issued so far has landed: the copies into
+        // bcur (issued one segment ago) and this segment's scales; its reads of
+        // bnext (previous segment) are done.
+        __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0)
+        if (more) {
+            // next segment: x first (split at the end of this one), then the
+            // scales, then the code copies, which stay in flight the longest
+            load_x<SB>(xs, x, M, K, b0 + SB, t);
+            scn = load_scales<SB>(sr, rows, C, b0 + SB);
+            stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, b0 + SB, bnext, lane);
+        }
 #pragma unroll
-        for (int j = 0; j < kSB; ++j) {
+        for (int j = 0; j < SB; ++j) {
             const int b = b0 + j;
             // this lane's x rows 8f + 4g .. 8f + 4g + 3: their factors of block j
             f4 ef[MF];
 #pragma unroll
             for (int f = 0; f < MF; ++f) ef[f] = *reinterpret_cast<const f4 *>(E + j * 16 + 8 * f + 4 * g);
             h8 bw[2];
-            unpack_codes<BITS>(cd[j], dc, dc5, bw);
-            const float sc = b < C ? (float)__builtin_bit_cast(_Float16, (uint16_t)cd[j].sc) : 0.0f;
-            // the next segment's codes for this slot, in flight during the rest
-            if (seg + 1 < nseg) {
-                const int bn = b + kSB < C ? b + kSB : C - 1;
-                cd[j] = load_codes<BITS>(qr, sr, rowq, hrow, rows, bn, g);
-            }
+            lane_codes<BITS, SB>(bcur, r, g, j, dc, dc5, bw);
+            const uint16_t sbits = (uint16_t)(scv.w[j >> 1] >> (16 * (j & 1)));
+            const float sc = b < C ? (float)__builtin_bit_cast(_Float16, sbits) : 0.0f;
 #pragma unroll
             for (int f = 0; f < MF; ++f) {
-                const uint8_t *op = buf + f * kOpBytes;
-                const h8 a0 = *reinterpret_cast<const h8 *>(op + aoff(r, j * 4 + 2 * g));
-                const h8 a1 = *reinterpret_cast<const h8 *>(op + aoff(r, j * 4 + 2 * g + 1));
+                const uint8_t *op = buf + f * A::OP_BYTES;
+                const h8 a0 = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, j * 4 + 2 * g));
+                const h8 a1 = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, j * 4 + 2 * g + 1));
                 f16v p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bw[0], zero, 0, 0, 0);
                 p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bw[1], p, 0, 0, 0);
                 // value v < 4 of lane (n, g): operand row 4g + v, i.e. x row
@@ -263,11 +346,17 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
                     asm volatile("" : "+v"(acc[f][v]));   // the block's scaling happens here
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);   // keep each block's work together (bounds live registers)
         }
-        if (seg + 1 < nseg) {
-            store_x<BITS, MF>(xs, M, lds + ((seg + 1) & 1) * Buf<MF>::BYTES, t);
-            lds_barrier();                       // the next buffer is complete, this one free; codes stay in flight
+        if (more) {
+            store_x<BITS, MF, SB>(xs, M, lds + ((seg + 1) & 1) * A::BYTES, t);
+            scv = scn;
+            lds_barrier();                       // the next operand buffer is complete, this one free
         }
+    };
+    for (int seg = 0; seg < nseg; seg += 2) {
+        segment(seg, w0, w1);
+        if (seg + 1 < nseg) segment(seg + 1, w1, w0);
     }
     if (nvalid) {
 #pragma unroll
@@ -285,15 +374,24 @@ __global__ __launch_bounds__(256) void mgemv_kernel(const float *__restrict__ x,
                                                     const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
                                                     float *__restrict__ y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Buf<MF>::BYTES];
-    mgemv_item<BITS, MF>(x, M, K, N, q, s, y, (int64_t)blockIdx.x * kMgemvRows, lds);
+    constexpr int SB = seg_blocks<BITS, MF>();
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Buf<MF, SB>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t bq0[BStage<BITS, SB>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t bq1[BStage<BITS, SB>::BYTES];
+    mgemv_item<BITS, MF>(x, M, K, N, q, s, y, (int64_t)blockIdx.x * kMgemvRows, lds, bq0, bq1);
 }
 
 template <int MF>
 __global__ __launch_bounds__(256) void mgemv_grouped_kernel(const uint8_t *__restrict__ base,
                                                             const wq_desc *__restrict__ table, int count, int M)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Buf<MF>::BYTES];
+    // buffers sized for the largest of the three code widths
+    constexpr int SB4 = seg_blocks<4, MF>(), SB8 = seg_blocks<8, MF>();
+    constexpr int AB = Buf<MF, SB4>::BYTES > Buf<MF, SB8>::BYTES ? Buf<MF, SB4>::BYTES : Buf<MF, SB8>::BYTES;
+    constexpr int B5 = BStage<5, SB4>::BYTES, B8 = BStage<8, SB8>::BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * AB];
+    __shared__ __attribute__((aligned(16))) uint8_t bq0[B5 > B8 ? B5 : B8];
+    __shared__ __attribute__((aligned(16))) uint8_t bq1[B5 > B8 ? B5 : B8];
     const int64_t item = blockIdx.x;
     int lo = 0, hi = count - 1;
     while (lo < hi) {
@@ -304,9 +402,9 @@ __global__ __launch_bounds__(256) void mgemv_grouped_kernel(const uint8_t *__res
     const uint8_t *q = base + d.q_off;
     const uint16_t *s = reinterpret_cast<const uint16_t *>(base + d.s_off);
     const int64_t row0 = (item - d.tile_begin) * kMgemvRows;
-    if (d.bits == 4) mgemv_item<4, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds);
-    else if (d.bits == 5) mgemv_item<5, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds);
-    else mgemv_item<8, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds);
+    if (d.bits == 4) mgemv_item<4, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq0, bq1);
+    else if (d.bits == 5) mgemv_item<5, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq0, bq1);
+    else mgemv_item<8, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq0, bq1);
 }
 
 }  // namespace
