@@ -4,16 +4,22 @@
 One step = one decode step of the Qwen3-0.6B-shaped decoder at M=1: the 197
 GEMVs (28 layers x q, k, v, o, gate, up, down in int4 block-32, plus the tied
 lm_head 1024->151936 in int8 block-32) as one grouped launch over a packed,
-64-byte-aligned tensor table, captured once in a HIP graph and replayed once
-per step, as a decode loop runs it. Inputs are resident in HBM before timing starts;
+64-byte-aligned tensor table, issued once per step as a decode loop issues it.
+Inputs are resident in HBM before timing starts;
 three package copies (1.24 GB) are rotated so every step streams its weights
 from HBM rather than from the 256 MB last-level cache.
 
-value = packed weight bytes (codes + binary16 scales) per step / step time.
+value = packed weight bytes (codes + binary16 scales) per step / step time
+(wall clock over K back-to-back steps, each step one grouped launch issued
+directly; the same step replayed from a HIP graph is reported beside it).
 Also reported: the roofline of the grouped GEMV kernel (algorithmic bytes per
-launch / mean launch time from HIP events on its stream), the CPU oracle timed
-on the host cores, and the prefill GEMM (M=4096 gate/up/down int4 + int8
-lm_head on the last 64 rows) in TFLOP/s against the fp16 matrix-core peak.
+launch / the kernel's duration, from HIP events on its stream around graphs of
+back-to-back launches), the CPU oracle timed on the host cores, and secondary
+legs: the sequential and fused (q|k|v, gate|up) forms of the step, tied-
+embedding lookups, batched decode of the mixed package at M=4 and 16, the int5
+step, and the prefill GEMM (M=4096 gate/up/down int4 + int8 lm_head on the
+last 64 rows) in TFLOP/s against the fp16 matrix-core peak. --decode-only
+runs the decode-step leg alone (the profile counter runs use it).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -73,6 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM leg")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode-step leg (the profile counter runs use this)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration runs)")
     return ap.parse_args()
@@ -253,6 +261,27 @@ def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
     return out
 
 
+def mixed_leg(torch, wqa, inputs, np, oracle, steps, warmup):
+    """Batched decode over the mixed package (attention int8, MLP int4, lm_head
+    int8), one grouped launch per step at M = 4 and 16 (M >= 3 runs on the
+    matrix cores)."""
+    out = {}
+    for M in (4, 16):
+        wl = inputs.decode_step(M, mixed=True)
+        pkgs, calls, ys, host_w, _ = build_decode(torch, wqa, wl, COPIES)
+        launch_ms, wall_ms = time_grouped(torch, calls, steps, warmup)
+        worst = check_outputs(wl, ys, host_w, np, oracle)
+        del pkgs, calls, ys
+        torch.cuda.empty_cache()
+        gbs = wl.total_bytes / (launch_ms * 1e-3) / 1e9
+        out[f"m{M}"] = {"ms_per_step": round(wall_ms, 5), "launch_ms": round(launch_ms, 5),
+                        "weight_gbs": round(wl.weight_bytes / (wall_ms * 1e-3) / 1e9, 1),
+                        "algorithmic_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "worst_err_over_bound": round(worst, 4)}
+    out["workload"] = "decode_step_mixed (attention int8, MLP int4, lm_head int8), 197 GEMVs"
+    return out
+
+
 def int5_leg(torch, wqa, inputs, np, oracle, steps, warmup):
     """INT5 (f4): the decode step with every projection packed in int5 (lm_head
     int8) as one grouped launch, and the M=4096 gate projection in int5 through
@@ -347,10 +376,28 @@ def prefill_leg(torch, wqa, inputs, steps, warmup):
 
 
 def time_grouped(torch, calls, steps, warmup):
-    """Each copy's step (one grouped launch) is captured once in a HIP graph, as a
-    decode loop would run it; the timed region replays `steps` steps back to back,
-    rotating the copies. Returns (ms per launch from HIP events on the replay
-    stream, wall-clock ms per step)."""
+    """A step is one grouped launch (the whole decode step), issued directly on
+    the current stream as a decode loop issues it; the timed region runs `steps`
+    steps back to back, rotating the package copies. Returns (ms per step from
+    HIP events on that stream, wall-clock ms per step)."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        calls[i % len(calls)]()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
+
+
+def graph_step_ms(torch, calls, steps):
+    """The same step captured once per package copy in a HIP graph and replayed
+    once per step (graph-launch gaps included), HIP events per step."""
     graphs = []
     for c in calls:
         c()
@@ -364,18 +411,16 @@ def time_grouped(torch, calls, steps, warmup):
         torch.cuda.synchronize()
         graphs.append(g)
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
+    for i in range(3):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(steps):
         graphs[i % len(graphs)].replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
+    return ev0.elapsed_time(ev1) / steps
 
 
 def fused_leg(torch, wqa, inputs, np, oracle, steps, warmup):
@@ -425,7 +470,9 @@ def main() -> int:
     pkgs, calls, ys, host_w, np = build_decode(torch, wqa, wl, COPIES)
 
     log(f"timing {args.steps} decode steps")
-    launch_ms, ms_per_step = time_grouped(torch, calls, args.steps, args.warmup)
+    step_ms, ms_per_step = time_grouped(torch, calls, args.steps, args.warmup)
+    launch_ms = step_ms
+    graph_ms = graph_step_ms(torch, calls, args.steps)
     value = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = wl.total_bytes / (launch_ms * 1e-3) / 1e9
     traffic = read_traffic()
@@ -433,10 +480,12 @@ def main() -> int:
     import oracle
     worst = check_outputs(wl, ys, host_w, np, oracle)
     log(f"timed outputs checked (worst err/bound {worst:.3f})")
-    log("sequential form (hipGraph of 197 launches)")
-    seq = sequential_leg(torch, wqa, wl, pkgs, np, max(10, args.steps // 4))
-    log("tied-embedding lookups")
-    emb = embed_leg(torch, wqa, wl, pkgs[0], host_w, np, oracle)
+    seq = emb = None
+    if not args.decode_only:
+        log("sequential form (hipGraph of 197 launches)")
+        seq = sequential_leg(torch, wqa, wl, pkgs, np, max(10, args.steps // 4))
+        log("tied-embedding lookups")
+        emb = embed_leg(torch, wqa, wl, pkgs[0], host_w, np, oracle)
     del pkgs, calls, ys
     torch.cuda.empty_cache()
 
@@ -464,21 +513,26 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic) if traffic is not None else None),
                      "kernel": "gemv_grouped_kernel", "launch_ms": round(launch_ms, 5),
-                     "launch_ms_source": "HIP events around the K back-to-back launches, divided by K",
+                     "launch_ms_source": "HIP events on the launch stream around the timed region "
+                                         "(one grouped launch per step), divided by the steps",
+                     "step_graph_replay_ms": round(graph_ms, 5),
                      "bytes_per_launch": wl.total_bytes},
         "parity": {"timed_outputs": "copies bitwise equal; sampled rows within 1e-5*sum|x||w|",
                    "worst_err_over_bound": round(worst, 4)},
         "decode_step_sequential": seq,
         "embedding": emb,
     }
-    log("shared-input fusion (113 GEMVs)")
-    result["decode_step_fused"] = fused_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
-    log("int5 decode step and GEMM")
-    result["int5"] = int5_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
-    if not args.no_prefill:
+    if not args.decode_only:
+        log("shared-input fusion (113 GEMVs)")
+        result["decode_step_fused"] = fused_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
+        log("mixed package, batched decode (M = 4, 16)")
+        result["decode_step_mixed"] = mixed_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
+        log("int5 decode step and GEMM")
+        result["int5"] = int5_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
+    if not args.no_prefill and not args.decode_only:
         log("prefill leg")
         result["prefill"] = prefill_leg(torch, wqa, inputs, max(3, args.steps // 10), max(1, args.warmup // 10))
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.decode_only:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, oracle, np)
     print(json.dumps(result), flush=True)
