@@ -12,9 +12,12 @@ from HBM rather than from the 256 MB last-level cache.
 value = packed weight bytes (codes + binary16 scales) per step / step time
 (wall clock over K back-to-back steps, each step one grouped launch issued
 directly; the same step replayed from a HIP graph is reported beside it).
+The default warmup (500 steps, about 40 ms) brings the chip to its steady
+clock state under this load: after idle, the first few hundred back-to-back
+launches run up to 20% slower while the clocks settle.
 Also reported: the roofline of the grouped GEMV kernel (algorithmic bytes per
-launch / the kernel's duration, from HIP events on its stream around graphs of
-back-to-back launches), the CPU oracle timed on the host cores, and secondary
+launch / the kernel's duration, from HIP events on its stream around the timed
+region, one launch per step), the CPU oracle timed on the host cores, and secondary
 legs: the sequential and fused (q|k|v, gate|up) forms of the step, tied-
 embedding lookups, batched decode of the mixed package at M=4 and 16, the int5
 step, and the prefill GEMM (M=4096 gate/up/down int4 + int8 lm_head on the
@@ -75,8 +78,8 @@ def read_traffic():
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM leg")
     ap.add_argument("--decode-only", action="store_true",

@@ -26,13 +26,15 @@
 //    output is about 8 + K/32, far below the ~160 at which fp32 rounding could
 //    reach 1e-5 * sum |x||w|.
 //  * A workgroup of 4 wavefronts owns 128 consecutive weight rows (32 per
-//    wavefront, one matrix column each) for all K. Lane (n, g) of a wavefront
-//    loads codes 16g..16g+15 of every block of its row straight from HBM into
-//    registers (one segment of 8 blocks ahead, cached: the 8 loads of a segment
-//    share each row's cache lines); x of the next segment is loaded
-//    into registers while the current one is computed, then split into the
-//    other of two LDS buffers. The operand order of the 8 values of a k-group is
-//    the order the unpack produces, identical for x and the codes.
+//    wavefront, one matrix column each) for all K, walked in segments of 4 or 8
+//    blocks. Each wavefront copies its rows' codes of the next segment from HBM
+//    straight into a wave-private LDS buffer (direct-to-LDS buffer loads of
+//    whole cache lines, no registers), while x of the next segment is loaded
+//    into registers and the current segment is computed; x is then split into
+//    the other of two operand buffers. Lane (n, g) reads codes 16g..16g+15 of
+//    each block of its row from LDS and unpacks them in registers. The operand
+//    order of the 8 values of a k-group is the order the unpack produces,
+//    identical for x and the codes.
 //  * The operand rows are stored with a row-dependent XOR swizzle of their
 //    16-byte slots, so the 16 lanes of each 128-bit LDS read hit distinct banks.
 // x blocks whose largest magnitude is below 2^-112 lose relative precision (the
