@@ -26,7 +26,7 @@
 //    output is about 8 + K/32, far below the ~160 at which fp32 rounding could
 //    reach 1e-5 * sum |x||w|.
 //  * A workgroup of 4 wavefronts owns 128 consecutive weight rows (32 per
-//    wavefront, one matrix column each) for all K, walked in segments of 4 or 8
+//    wavefront, one matrix column each) for all K, walked in segments of 4
 //    blocks. Each wavefront copies its rows' codes of the next segment from HBM
 //    straight into a wave-private LDS buffer (direct-to-LDS buffer loads of
 //    whole cache lines, no registers), while x of the next segment is loaded
@@ -51,11 +51,12 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-// Blocks per segment: 8, or 4 for int8 codes and for M > 8, so that the
-// workgroup's LDS (two operand buffers and two code buffers) stays near 72 KiB
-// and two workgroups share a compute unit.
+// Blocks per segment: 4 for every code width. With at most 8 activation rows
+// the workgroup's LDS (two operand buffers and two code buffers) is then about
+// 49 KiB and three workgroups share a compute unit; 8-block segments for int4
+// (72 KiB, two workgroups) measured 6-7% slower at M = 4 and 8.
 template <int BITS, int MF>
-constexpr int seg_blocks() { return (MF == 1 && BITS != 8) ? 8 : 4; }
+constexpr int seg_blocks() { return 4; }
 
 // Operand buffer of a segment of SB blocks: MF 32-row operands (binary16, row
 // pitch SB * 64 bytes) and the factors 2^-e, [SB][16] floats.
