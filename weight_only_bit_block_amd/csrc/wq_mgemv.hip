@@ -130,26 +130,48 @@ __device__ __forceinline__ void stage_codes(__amdgpu_buffer_rsrc_t qr, uint32_t 
     }
 }
 
-// Lane (r, g): codes 16g .. 16g+15 of block j of its row, as two groups of 8 in
-// unpack order.
+// Lane (r, g)'s codes of a segment: codes 16g .. 16g+15 of each block of its
+// row, as raw packed words (int5: with their bit-4 bytes).
 template <int BITS, int SB>
-__device__ __forceinline__ void lane_codes(const uint8_t *src, int r, int g, int j, const DecodeConsts &dc,
-                                           const Decode5Consts &dc5, h8 (&b)[2])
+struct LaneCodes {
+    u4 v[BITS == 8 ? SB : (SB + 1) / 2];   // int8: 16 bytes per block; int4/int5: 8 bytes per block
+    uint32_t h[SB];                        // int5: bit 4 of the 16 codes of each block
+};
+
+template <int BITS, int SB>
+__device__ __forceinline__ void read_codes(const uint8_t *src, int r, int g, LaneCodes<BITS, SB> &c)
 {
     using B = BStage<BITS, SB>;
-    if constexpr (BITS == 8) {
-        const u4 v = *reinterpret_cast<const u4 *>(src + r * B::ROW + ((2 * j + g) ^ B::swz(r)) * 16);
-        b[0] = unpack8_int8(v.x, v.y, dc);
-        b[1] = unpack8_int8(v.z, v.w, dc);
-    } else {
-        const u2 v = *reinterpret_cast<const u2 *>(src + r * B::ROW + (j ^ B::swz(r)) * 16 + g * 8);
-        if constexpr (BITS == 4) {
-            b[0] = unpack8_int4(v.x, dc);
-            b[1] = unpack8_int4(v.y, dc);
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        if constexpr (BITS == 8) {
+            c.v[j] = *reinterpret_cast<const u4 *>(src + r * B::ROW + ((2 * j + g) ^ B::swz(r)) * 16);
         } else {
-            const uint32_t h = *reinterpret_cast<const uint16_t *>(src + B::CODE_BYTES + r * (SB * 4) + j * 4 + g * 2);
-            b[0] = unpack8_int5(v.x, h & 0xFF, dc5);
-            b[1] = unpack8_int5(v.y, h >> 8, dc5);
+            const u2 v = *reinterpret_cast<const u2 *>(src + r * B::ROW + (j ^ B::swz(r)) * 16 + g * 8);
+            c.v[j / 2][2 * (j & 1)] = v.x;
+            c.v[j / 2][2 * (j & 1) + 1] = v.y;
+            if constexpr (BITS == 5)
+                c.h[j] = *reinterpret_cast<const uint16_t *>(src + B::CODE_BYTES + r * (SB * 4) + j * 4 + g * 2);
+        }
+    }
+}
+
+// Block j of a lane's segment codes as two groups of 8 in unpack order.
+template <int BITS, int SB>
+__device__ __forceinline__ void lane_codes(const LaneCodes<BITS, SB> &c, int j, const DecodeConsts &dc,
+                                           const Decode5Consts &dc5, h8 (&b)[2])
+{
+    if constexpr (BITS == 8) {
+        b[0] = unpack8_int8(c.v[j].x, c.v[j].y, dc);
+        b[1] = unpack8_int8(c.v[j].z, c.v[j].w, dc);
+    } else {
+        const uint32_t lo = c.v[j / 2][2 * (j & 1)], hi = c.v[j / 2][2 * (j & 1) + 1];
+        if constexpr (BITS == 4) {
+            b[0] = unpack8_int4(lo, dc);
+            b[1] = unpack8_int4(hi, dc);
+        } else {
+            b[0] = unpack8_int5(lo, c.h[j] & 0xFF, dc5);
+            b[1] = unpack8_int5(hi, c.h[j] >> 8, dc5);
         }
     }
 }
@@ -258,13 +280,15 @@ __device__ __forceinline__ void store_x(const XStage<SB> &xs, int M, uint8_t *bu
 }
 
 // One item: weight rows row0 .. row0+127 of one tensor, all M activation rows
-// (M <= 8 * MF). bq0 / bq1: the two LDS buffers of the codes (separate arrays,
-// so reading one never waits for copies into the other).
+// (M <= 8 * MF). bq: the LDS buffer of the codes (a separate array, so reads of
+// the operand buffers never wait for copies into it). Each wavefront moves its
+// codes of a segment from bq into registers when the segment starts, so the
+// same buffer then takes the next segment's copies.
 template <int BITS, int MF>
 __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, int K, int64_t N,
                                            const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
                                            float *__restrict__ y, int64_t row0, uint8_t *__restrict__ lds,
-                                           uint8_t *__restrict__ bq0, uint8_t *__restrict__ bq1)
+                                           uint8_t *__restrict__ bq)
 {
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -286,8 +310,7 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
     const bool nvalid = n < N;
     n = nvalid ? n : N - 1;                      // rows past N reload the last row, not stored
     const uint32_t rows = (uint32_t)n * C * 2;
-    uint8_t *const w0 = bq0 + wave * BS::WAVE_BYTES;
-    uint8_t *const w1 = bq1 + wave * BS::WAVE_BYTES;
+    uint8_t *const wq = bq + wave * BS::WAVE_BYTES;
 
     float acc[MF][4];
 #pragma unroll
@@ -299,28 +322,31 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
     XStage<SB> xs;
     Scales<SB> scv = load_scales<SB>(sr, rows, C, 0), scn = scv;
     // prologue: segment 0's codes copied, its x split into buffer 0
-    stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, 0, w0, lane);
+    stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, 0, wq, lane);
     load_x<SB>(xs, x, M, K, 0, t);
     store_x<BITS, MF, SB>(xs, M, lds, t);
     lds_barrier();
 
-    // One segment: codes from bcur; the next segment's codes into bnext and its
-    // x into the other operand buffer.
-    auto segment = [&](int seg, const uint8_t *bcur, uint8_t *bnext) {
+    // One segment: codes from the buffer into registers, then the next
+    // segment's codes into the buffer and its x into the other operand buffer.
+    auto segment = [&](int seg) {
         const int b0 = seg * SB;
         const uint8_t *buf = lds + (seg & 1) * A::BYTES;
         const float *E = reinterpret_cast<const float *>(buf + A::A_BYTES);
         const bool more = seg + 1 < nseg;
-        // Everything this wavefront issued so far has landed: the copies into
-        // bcur (issued one segment ago) and this segment's scales; its reads of
-        // bnext (previous segment) are done.
+        // Everything this wavefront issued so far has landed: the copies of this
+        // segment's codes (issued one segment ago) and its scales.
         __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0)
+        LaneCodes<BITS, SB> lc;
+        read_codes<BITS, SB>(wq, r, g, lc);
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the reads are done, the buffer is free
+        asm volatile("" ::: "memory");
         if (more) {
             // next segment: x first (split at the end of this one), then the
             // scales, then the code copies, which stay in flight the longest
             load_x<SB>(xs, x, M, K, b0 + SB, t);
             scn = load_scales<SB>(sr, rows, C, b0 + SB);
-            stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, b0 + SB, bnext, lane);
+            stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, b0 + SB, wq, lane);
         }
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
@@ -330,7 +356,7 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
 #pragma unroll
             for (int f = 0; f < MF; ++f) ef[f] = *reinterpret_cast<const f4 *>(E + j * 16 + 8 * f + 4 * g);
             h8 bw[2];
-            lane_codes<BITS, SB>(bcur, r, g, j, dc, dc5, bw);
+            lane_codes<BITS, SB>(lc, j, dc, dc5, bw);
             const uint16_t sbits = (uint16_t)(scv.w[j >> 1] >> (16 * (j & 1)));
             const float sc = b < C ? (float)__builtin_bit_cast(_Float16, sbits) : 0.0f;
 #pragma unroll
@@ -357,10 +383,7 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
             lds_barrier();                       // the next operand buffer is complete, this one free
         }
     };
-    for (int seg = 0; seg < nseg; seg += 2) {
-        segment(seg, w0, w1);
-        if (seg + 1 < nseg) segment(seg + 1, w1, w0);
-    }
+    for (int seg = 0; seg < nseg; ++seg) segment(seg);
     if (nvalid) {
 #pragma unroll
         for (int f = 0; f < MF; ++f)
@@ -379,9 +402,8 @@ __global__ __launch_bounds__(256) void mgemv_kernel(const float *__restrict__ x,
 {
     constexpr int SB = seg_blocks<BITS, MF>();
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Buf<MF, SB>::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t bq0[BStage<BITS, SB>::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t bq1[BStage<BITS, SB>::BYTES];
-    mgemv_item<BITS, MF>(x, M, K, N, q, s, y, (int64_t)blockIdx.x * kMgemvRows, lds, bq0, bq1);
+    __shared__ __attribute__((aligned(16))) uint8_t bq[BStage<BITS, SB>::BYTES];
+    mgemv_item<BITS, MF>(x, M, K, N, q, s, y, (int64_t)blockIdx.x * kMgemvRows, lds, bq);
 }
 
 template <int MF>
@@ -393,8 +415,7 @@ __global__ __launch_bounds__(256) void mgemv_grouped_kernel(const uint8_t *__res
     constexpr int AB = Buf<MF, SB4>::BYTES > Buf<MF, SB8>::BYTES ? Buf<MF, SB4>::BYTES : Buf<MF, SB8>::BYTES;
     constexpr int B5 = BStage<5, SB4>::BYTES, B8 = BStage<8, SB8>::BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * AB];
-    __shared__ __attribute__((aligned(16))) uint8_t bq0[B5 > B8 ? B5 : B8];
-    __shared__ __attribute__((aligned(16))) uint8_t bq1[B5 > B8 ? B5 : B8];
+    __shared__ __attribute__((aligned(16))) uint8_t bq[B5 > B8 ? B5 : B8];
     const int64_t item = blockIdx.x;
     int lo = 0, hi = count - 1;
     while (lo < hi) {
@@ -405,9 +426,9 @@ __global__ __launch_bounds__(256) void mgemv_grouped_kernel(const uint8_t *__res
     const uint8_t *q = base + d.q_off;
     const uint16_t *s = reinterpret_cast<const uint16_t *>(base + d.s_off);
     const int64_t row0 = (item - d.tile_begin) * kMgemvRows;
-    if (d.bits == 4) mgemv_item<4, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq0, bq1);
-    else if (d.bits == 5) mgemv_item<5, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq0, bq1);
-    else mgemv_item<8, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq0, bq1);
+    if (d.bits == 4) mgemv_item<4, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
+    else if (d.bits == 5) mgemv_item<5, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
+    else mgemv_item<8, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
 }
 
 }  // namespace
