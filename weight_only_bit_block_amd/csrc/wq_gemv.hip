@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
                                                            float *__restrict__ y)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const GemvGeom g = gemv_geom(K, BITS, N, false);
+    const GemvGeom g = gemv_geom(K, BITS, N, false, MT);
     const int64_t row0 = (int64_t)blockIdx.x * g.rows;
     if constexpr (S == 0) gemv_item_general<BITS, MT, MLOOP>(x, M, K, N, q, s, y, row0, g, lds);
     else gemv_item_fast<BITS, MT, J, S, MLOOP>(x, M, K, N, q, s, y, row0, g.CPL, lds);
@@ -508,7 +508,7 @@ __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint
                                              const uint16_t *__restrict__ s, int64_t item, uint8_t *lds)
 {
     const int K = (int)d.K;
-    const GemvGeom g = gemv_geom(K, BITS, d.N, true);
+    const GemvGeom g = gemv_geom(K, BITS, d.N, true, MT);
     const int64_t row0 = item * g.rows;
     // int5 with 4 activation rows in registers (3 or 4 rows, one pass): the fast
     // forms' chunks plus their bit-4 dwords would not fit the grouped kernel's
@@ -574,7 +574,7 @@ template <int BITS, int MT, bool MLOOP>
 hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                           const uint16_t *s, float *y, hipStream_t stream)
 {
-    const GemvGeom g = gemv_geom(K, BITS, N, false);
+    const GemvGeom g = gemv_geom(K, BITS, N, false, MT);
     {
         switch (g.kind) {
         case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);

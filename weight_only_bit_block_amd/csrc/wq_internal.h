@@ -47,8 +47,12 @@ struct GemvGeom {
 };
 
 // Single launches with few items use one row per lane to spread over the chip;
-// the grouped launch always uses the same shape for a given (K, bits).
-__host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bool grouped)
+// the grouped launch always uses the same shape for a given (K, bits, mt).
+// With two activation rows (mt == 2) every fast shape takes two rows per lane
+// in segments of two chunks: each staged x piece read from LDS then serves two
+// weight rows, which halves the LDS reads of x that bound that case. J and S
+// never change the arithmetic of an output (it depends on K and bits only).
+__host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bool grouped, int mt = 1)
 {
     GemvGeom g;
     const int cpb = bits / 4;
@@ -63,7 +67,7 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
     g.kind = kGemvGeneral;
     if (G == 16 && K % 256 == 0) {
         const int64_t rows_j2 = (int64_t)kGemvWaves * 4 * 2;
-        if (g.CPL == 2) {
+        if (g.CPL == 2 || (mt == 2 && g.CPL % 2 == 0)) {
             const bool few = !grouped && (N + rows_j2 - 1) / rows_j2 < 256;
             g.kind = few ? kGemvJ1S2 : kGemvJ2S2;
             g.J = few ? 1 : 2;
@@ -93,14 +97,14 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
 constexpr int kMgemvRows = 128;
 constexpr int kMgemvMinM = 3;
 
+// Activation rows staged at once (m-group size): 1, 2 or 4.
+__host__ __device__ inline int gemv_mt(int64_t M) { return M <= 2 ? (int)M : kGemvMaxMT; }
+
 // Rows per work item of a decode call with M activation rows.
 __host__ __device__ inline int64_t decode_item_rows(int64_t K, int bits, int64_t N, bool grouped, int64_t M)
 {
-    return M >= kMgemvMinM ? (int64_t)kMgemvRows : gemv_geom(K, bits, N, grouped).rows;
+    return M >= kMgemvMinM ? (int64_t)kMgemvRows : gemv_geom(K, bits, N, grouped, gemv_mt(M)).rows;
 }
-
-// Activation rows staged at once (m-group size): 1, 2 or 4.
-__host__ __device__ inline int gemv_mt(int64_t M) { return M <= 2 ? (int)M : kGemvMaxMT; }
 
 // LDS of an item: MT staged x rows (128 bytes per block) and, in the fast form,
 // the item's scales for one segment.
