@@ -521,6 +521,10 @@ __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint
             if (r > 0) copies_barrier<0>();       // the first pass's LDS readers are done
             gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0 + r, g, lds);
         }
+    } else if constexpr (MT <= 2) {
+        // the shapes gemv_geom gives a grouped launch with one or two rows
+        if (g.kind == kGemvJ2S2) gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+        else gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
     } else {
         switch (g.kind) {
         case kGemvJ2S2: gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
@@ -575,7 +579,14 @@ hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const
                           const uint16_t *s, float *y, hipStream_t stream)
 {
     const GemvGeom g = gemv_geom(K, BITS, N, false, MT);
-    {
+    if constexpr (MT <= 2) {
+        // the shapes gemv_geom gives a single launch with one or two rows
+        switch (g.kind) {
+        case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
+        }
+    } else {
         switch (g.kind) {
         case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
         case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
