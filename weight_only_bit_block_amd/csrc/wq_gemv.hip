@@ -1,4 +1,5 @@
-// wq_gemv.hip -- decode GEMV for block-32 int4 / int5 / int8 weights, 1 <= M <= 16.
+// wq_gemv.hip -- decode GEMV for block-32 int4 / int5 / int8 weights, M <= 2
+// activation rows (3 <= M <= 16 run on the matrix cores, wq_mgemv.hip).
 //
 // The devpost page for TinyMOSS-Diarize ("How we built it") describes a
 // separate GEMV path for decode that multiplies straight out of the packed
@@ -11,12 +12,12 @@
 //    wavefront share a row and each lane owns the 16-byte chunks li, li+G,
 //    li+2G, ... of it (one int4 block, or half an int8 block, per chunk), so
 //    the lanes of a row read G*16 contiguous bytes per load (geometry in
-//    wq_internal.h). The item's codes are loaded up front with non-temporal
-//    128-bit loads straight into registers: every byte of the item is in
-//    flight at once, and memory and arithmetic overlap across the many items
-//    resident on each compute unit (few registers per lane, so many items).
-//    Items are small (16-24 KiB of codes at the decoder's shapes), so a launch
-//    has tens of thousands of them and its tail is short.
+//    wq_internal.h). In the fast form a lane owns four rows and walks them in
+//    segments of two chunks per row: the segment's eight chunks are loaded with
+//    non-temporal 128-bit loads straight into registers, and memory and
+//    arithmetic overlap across the many items resident on each compute unit.
+//    Items hold 32-128 KiB of codes at the decoder's shapes, so a launch has
+//    thousands of them and its tail is short.
 //  * x and the item's scales are copied into LDS by direct-to-LDS loads
 //    (global_load_lds_dwordx4: no registers), issued before the code loads; a
 //    barrier that waits only for those copies lets the code loads stay in
@@ -45,11 +46,6 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float fmix(_Float16 w, float x, float acc)
-{
-    return __builtin_fmaf((float)w, x, acc);   // one v_fma_mix_f32: exact product, one rounding
-}
 
 // A code as fp32 (exact). With one activation row the conversion folds into
 // v_fma_mix_f32; with several, each code is converted once and the MT products
@@ -315,9 +311,8 @@ __device__ __forceinline__ void reduce_store(float (&acc)[J][MT], int G, int li,
 // Fast item form: G == 16 and K % 256 == 0. The row is walked in CPL/S full
 // segments of S chunks per lane; per segment the x blocks and the item's scales
 // are copied into LDS, then the J*S code loads are issued, and the barrier
-// waits for the copies only. With MLOOP the M activation rows are taken MT at a
-// time; without it, M <= MT and there is one pass.
-template <int BITS, int MT, int J, int S, bool MLOOP>
+// waits for the copies only. All M <= MT activation rows in one pass.
+template <int BITS, int MT, int J, int S>
 __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int M, int K, int64_t N,
                                                const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
                                                float *__restrict__ y, int64_t row0, int CPL,
@@ -351,48 +346,40 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
 
     u4 w[J][S];
     uint32_t hw[J][S];                          // int5: the chunks' bit-4 dwords
-    const int mend = MLOOP ? M : 1;            // without MLOOP, M <= MT: one pass
-    for (int mg = 0; mg < mend; mg += MT) {
-        float acc[J][MT];
+    float acc[J][MT];
 #pragma unroll
-        for (int j = 0; j < J; ++j)
+    for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
+        for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
+    {
         for (int seg = 0; seg < nseg; ++seg) {
             const int b0 = seg * NB;
-            if (mg > 0 || seg > 0) copies_barrier<0>();                // earlier readers of LDS are done
-            const bool codes = mg == 0 || nseg > 1;
-            if (codes) {
-                // the item's scales for the segment: IROWS rows of NB binary16 values
-                copy_pieces(IROWS * NB / 8, reinterpret_cast<uint8_t *>(ss), wave, lane, [&](int pc) {
-                    const int r = pc / (NB / 8);
-                    const int k8 = pc - r * (NB / 8);
-                    int64_t row = row0 + r;
-                    row = row < N ? row : N - 1;
-                    return reinterpret_cast<const uint8_t *>(s + (size_t)row * C + b0 + k8 * 8);
-                });
-            }
-            stage_x<MT>(x, M, K, mg, b0, NB, xs, wave, lane);
-            if (codes) {
+            if (seg > 0) copies_barrier<0>();                          // earlier readers of LDS are done
+            // the item's scales for the segment: IROWS rows of NB binary16 values
+            copy_pieces(IROWS * NB / 8, reinterpret_cast<uint8_t *>(ss), wave, lane, [&](int pc) {
+                const int r = pc / (NB / 8);
+                const int k8 = pc - r * (NB / 8);
+                int64_t row = row0 + r;
+                row = row < N ? row : N - 1;
+                return reinterpret_cast<const uint8_t *>(s + (size_t)row * C + b0 + k8 * 8);
+            });
+            stage_x<MT>(x, M, K, 0, b0, NB, xs, wave, lane);
+#pragma unroll
+            for (int c = 0; c < S; ++c)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    w[j][c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         qr, rowq[j] + (uint32_t)((seg * S + c) * G + li) * 16,
+                                                         0, kNonTemporal));
+            if constexpr (BITS == 5) {
 #pragma unroll
                 for (int c = 0; c < S; ++c)
 #pragma unroll
                     for (int j = 0; j < J; ++j)
-                        w[j][c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                             qr, rowq[j] + (uint32_t)((seg * S + c) * G + li) * 16,
-                                                             0, kNonTemporal));
-                if constexpr (BITS == 5) {
-#pragma unroll
-                    for (int c = 0; c < S; ++c)
-#pragma unroll
-                        for (int j = 0; j < J; ++j)
-                            hw[j][c] = __builtin_amdgcn_raw_buffer_load_b32(
-                                qr, rowq[j] + (uint32_t)K / 2 + (uint32_t)((seg * S + c) * G + li) * 4, 0, kNonTemporal);
-                }
-                copies_barrier<NL>();                                    // codes stay in flight
-            } else {
-                copies_barrier<0>();
+                        hw[j][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                            qr, rowq[j] + (uint32_t)K / 2 + (uint32_t)((seg * S + c) * G + li) * 4, 0, kNonTemporal);
             }
+            copies_barrier<NL>();                                        // codes stay in flight
             // Lane li reads block blk(c) = c * 16 / CPB + blk0 of the segment; the
             // swizzle of its pieces depends on li only (int4) or on li and the parity
             // of c (int8), so the piece pointers are set once and each chunk adds a
@@ -422,13 +409,13 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
                 __builtin_amdgcn_sched_barrier(0);   // keep each chunk's work together (bounds live registers)
             }
         }
-        reduce_store<MT, J>(acc, G, li, row0 + lrow0, N, mg, M, y);
+        reduce_store<MT, J>(acc, G, li, row0 + lrow0, N, 0, M, y);
     }
 }
 
 // General item form (any K % 32 == 0): one row per lane, chunk by chunk. x is
 // staged per segment of up to kGemvGenBlocks blocks; scales are read directly.
-template <int BITS, int MT, bool MLOOP>
+template <int BITS, int MT>
 __device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, int M, int K, int64_t N,
                                                   const uint8_t *__restrict__ q,
                                                   const uint16_t *__restrict__ s, float *__restrict__ y,
@@ -454,16 +441,15 @@ __device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, i
     r = r < N ? r : N - 1;
     const uint32_t rq = (uint32_t)r * qrow, rs = (uint32_t)r * (uint32_t)C * 2;
     const int seg_chunks = g.nb * CPB;         // chunks of a row per segment (x blocks staged at once)
-    const int mend = MLOOP ? M : 1;
-    for (int mg = 0; mg < mend; mg += MT) {
+    {
         float acc[1][MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[0][m] = 0.0f;
         for (int c0 = 0; c0 < CC; c0 += seg_chunks) {
             const int b0 = c0 / CPB;
             const int nbs = ((CC - c0) < seg_chunks ? (CC - c0) : seg_chunks) / CPB;
-            if (mg > 0 || c0 > 0) copies_barrier<0>();
-            stage_x<MT>(x, M, K, mg, b0, nbs, lds, wave, lane);
+            if (c0 > 0) copies_barrier<0>();
+            stage_x<MT>(x, M, K, 0, b0, nbs, lds, wave, lane);
             copies_barrier<0>();
 #pragma unroll 1
             for (int ch = c0 + li; ch < c0 + nbs * CPB; ch += G) {
@@ -484,68 +470,44 @@ __device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, i
                 }
             }
         }
-        reduce_store<MT, 1>(acc, G, li, row0 + lrow, N, mg, M, y);
+        reduce_store<MT, 1>(acc, G, li, row0 + lrow, N, 0, M, y);
     }
 }
 
-template <int BITS, int MT, int J, int S, bool MLOOP>
+template <int BITS, int MT, int J, int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restrict__ x, int M, int K, int64_t N,
                                                            const uint8_t *__restrict__ q,
                                                            const uint16_t *__restrict__ s,
                                                            float *__restrict__ y)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const GemvGeom g = gemv_geom(K, BITS, N, false, MT);
+    const GemvGeom g = gemv_geom(K, BITS, N, false);
     const int64_t row0 = (int64_t)blockIdx.x * g.rows;
-    if constexpr (S == 0) gemv_item_general<BITS, MT, MLOOP>(x, M, K, N, q, s, y, row0, g, lds);
-    else gemv_item_fast<BITS, MT, J, S, MLOOP>(x, M, K, N, q, s, y, row0, g.CPL, lds);
+    if constexpr (S == 0) gemv_item_general<BITS, MT>(x, M, K, N, q, s, y, row0, g, lds);
+    else gemv_item_fast<BITS, MT, J, S>(x, M, K, N, q, s, y, row0, g.CPL, lds);
 }
 
 // Grouped launch: workgroup b computes item b - tile_begin of the last table
 // entry whose tile_begin <= b.
-template <int BITS, int MT, bool MLOOP>
+template <int BITS, int MT>
 __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint8_t *__restrict__ q,
                                              const uint16_t *__restrict__ s, int64_t item, uint8_t *lds)
 {
     const int K = (int)d.K;
-    const GemvGeom g = gemv_geom(K, BITS, d.N, true, MT);
+    const GemvGeom g = gemv_geom(K, BITS, d.N, true);
     const int64_t row0 = item * g.rows;
-    // int5 with 4 activation rows in registers (3 or 4 rows, one pass): the fast
-    // forms' chunks plus their bit-4 dwords would not fit the grouped kernel's
-    // register bound, so these items take the general form (one row per lane,
-    // the same arithmetic and results), twice when the item holds two rows per
-    // lane.
-    if constexpr (BITS == 5 && MT == 4 && !MLOOP) {
-        const int64_t half = (int64_t)kGemvWaves * (kWave / g.G);
-        for (int64_t r = 0; r < g.rows; r += half) {
-            if (r > 0) copies_barrier<0>();       // the first pass's LDS readers are done
-            gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0 + r, g, lds);
-        }
-    } else if constexpr (MT <= 2) {
-        // the shapes gemv_geom gives a grouped launch with one or two rows
-        if (g.kind == kGemvJ2S2) gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
-        else gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
-    } else {
-        switch (g.kind) {
-        case kGemvJ2S2: gemv_item_fast<BITS, MT, 2, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
-        case kGemvJ1S2: gemv_item_fast<BITS, MT, 1, 2, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
-        case kGemvJ1S4: gemv_item_fast<BITS, MT, 1, 4, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds); break;
-        case kGemvJ1S6:
-        case kGemvJ1S8:
-            gemv_item_fast<BITS, MT, 1, BITS == 8 ? 8 : 6, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
-            break;
-        default: gemv_item_general<BITS, MT, MLOOP>(d.x, M, K, d.N, q, s, d.y, row0, g, lds); break;
-        }
-    }
+    // the shapes gemv_geom gives a grouped launch
+    if (g.kind == kGemvJ4S2) gemv_item_fast<BITS, MT, 4, 2>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+    else gemv_item_general<BITS, MT>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
 }
 
 // Wavefronts per SIMD the grouped kernel is compiled for: the kernel holds every
 // item form, and without a bound its registers follow the largest of them.
-template <int MT, bool MLOOP>
-constexpr int grouped_waves_per_simd() { return MLOOP ? 4 : MT == 1 ? 7 : MT == 2 ? 6 : 5; }
+template <int MT>
+constexpr int grouped_waves_per_simd() { return MT == 1 ? 5 : 4; }
 
-template <int MT, bool MLOOP>
-__global__ __launch_bounds__(kGemvThreads, (grouped_waves_per_simd<MT, MLOOP>())) void gemv_grouped_kernel(const uint8_t *__restrict__ base,
+template <int MT>
+__global__ __launch_bounds__(kGemvThreads, (grouped_waves_per_simd<MT>())) void gemv_grouped_kernel(const uint8_t *__restrict__ base,
                                                                    const wq_desc *__restrict__ table,
                                                                    int count, int M)
 {
@@ -559,42 +521,30 @@ __global__ __launch_bounds__(kGemvThreads, (grouped_waves_per_simd<MT, MLOOP>())
     const wq_desc d = table[lo];
     const uint8_t *q = base + d.q_off;
     const uint16_t *s = reinterpret_cast<const uint16_t *>(base + d.s_off);
-    if (d.bits == 4) grouped_item<4, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
-    else if (d.bits == 5) grouped_item<5, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
-    else grouped_item<8, MT, MLOOP>(d, M, q, s, item - d.tile_begin, lds);
+    if (d.bits == 4) grouped_item<4, MT>(d, M, q, s, item - d.tile_begin, lds);
+    else if (d.bits == 5) grouped_item<5, MT>(d, M, q, s, item - d.tile_begin, lds);
+    else grouped_item<8, MT>(d, M, q, s, item - d.tile_begin, lds);
 }
 
-template <int BITS, int MT, int J, int S, bool MLOOP>
+template <int BITS, int MT, int J, int S>
 hipError_t launch_kind(const float *x, int64_t M, int64_t K, int64_t N, const void *q, const uint16_t *s,
                        float *y, const GemvGeom &g, hipStream_t stream)
 {
     const int64_t items = (N + g.rows - 1) / g.rows;
-    gemv_kernel<BITS, MT, J, S, MLOOP><<<(unsigned)items, kGemvThreads, gemv_lds_bytes(MT, g), stream>>>(
+    gemv_kernel<BITS, MT, J, S><<<(unsigned)items, kGemvThreads, gemv_lds_bytes(MT, g), stream>>>(
         x, (int)M, (int)K, N, (const uint8_t *)q, s, y);
     return hipGetLastError();
 }
 
-template <int BITS, int MT, bool MLOOP>
+template <int BITS, int MT>
 hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                           const uint16_t *s, float *y, hipStream_t stream)
 {
-    const GemvGeom g = gemv_geom(K, BITS, N, false, MT);
-    if constexpr (MT <= 2) {
-        // the shapes gemv_geom gives a single launch with one or two rows
-        switch (g.kind) {
-        case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        }
-    } else {
-        switch (g.kind) {
-        case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        case kGemvJ1S4: return launch_kind<BITS, MT, 1, 4, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        case kGemvJ1S6:
-        case kGemvJ1S8: return launch_kind<BITS, MT, 1, BITS == 8 ? 8 : 6, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        default: return launch_kind<BITS, MT, 1, 0, MLOOP>(x, M, K, N, q, s, y, g, stream);
-        }
+    const GemvGeom g = gemv_geom(K, BITS, N, false);
+    switch (g.kind) {
+    case kGemvJ4S2: return launch_kind<BITS, MT, 4, 2>(x, M, K, N, q, s, y, g, stream);
+    case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2>(x, M, K, N, q, s, y, g, stream);
+    default: return launch_kind<BITS, MT, 1, 0>(x, M, K, N, q, s, y, g, stream);
     }
 }
 
@@ -602,20 +552,15 @@ template <int BITS>
 hipError_t launch_gemv_bits(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                             const uint16_t *s, float *y, hipStream_t stream)
 {
-    switch (gemv_mt(M)) {
-    case 1: return launch_gemv_mt<BITS, 1, false>(x, M, K, N, q, s, y, stream);
-    case 2: return launch_gemv_mt<BITS, 2, false>(x, M, K, N, q, s, y, stream);
-    default:
-        if (M <= kGemvMaxMT) return launch_gemv_mt<BITS, 4, false>(x, M, K, N, q, s, y, stream);
-        return launch_gemv_mt<BITS, 4, true>(x, M, K, N, q, s, y, stream);
-    }
+    if (M == 1) return launch_gemv_mt<BITS, 1>(x, M, K, N, q, s, y, stream);
+    return launch_gemv_mt<BITS, 2>(x, M, K, N, q, s, y, stream);
 }
 
-template <int MT, bool MLOOP>
-hipError_t launch_grouped_mt(const void *base, const wq_desc *table, int count, int64_t items,
-                             int64_t M, hipStream_t stream)
+template <int MT>
+hipError_t launch_grouped_mt(const void *base, const wq_desc *table, int count, int64_t items, int64_t M,
+                             hipStream_t stream)
 {
-    gemv_grouped_kernel<MT, MLOOP><<<(unsigned)items, kGemvThreads, gemv_lds_bytes_max(MT), stream>>>(
+    gemv_grouped_kernel<MT><<<(unsigned)items, kGemvThreads, gemv_lds_bytes_max(MT), stream>>>(
         (const uint8_t *)base, table, count, (int)M);
     return hipGetLastError();
 }
@@ -625,6 +570,7 @@ hipError_t launch_grouped_mt(const void *base, const wq_desc *table, int count, 
 hipError_t launch_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
+    if (M < 1 || M > kGemvMaxMT) return hipErrorInvalidValue;   // 3 <= M goes to the matrix-core kernel
     if (bits == 4) return launch_gemv_bits<4>(x, M, K, N, q, scales, y, stream);
     if (bits == 5) return launch_gemv_bits<5>(x, M, K, N, q, scales, y, stream);
     return launch_gemv_bits<8>(x, M, K, N, q, scales, y, stream);
@@ -633,13 +579,9 @@ hipError_t launch_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits
 hipError_t launch_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
                                int64_t total_items, int64_t M, hipStream_t stream)
 {
-    switch (gemv_mt(M)) {
-    case 1: return launch_grouped_mt<1, false>(base, table_dev, count, total_items, M, stream);
-    case 2: return launch_grouped_mt<2, false>(base, table_dev, count, total_items, M, stream);
-    default:
-        if (M <= kGemvMaxMT) return launch_grouped_mt<4, false>(base, table_dev, count, total_items, M, stream);
-        return launch_grouped_mt<4, true>(base, table_dev, count, total_items, M, stream);
-    }
+    if (M < 1 || M > kGemvMaxMT) return hipErrorInvalidValue;
+    if (M == 1) return launch_grouped_mt<1>(base, table_dev, count, total_items, M, stream);
+    return launch_grouped_mt<2>(base, table_dev, count, total_items, M, stream);
 }
 
 }  // namespace wq

@@ -24,17 +24,20 @@ constexpr int kWave = 64;           // gfx950 wavefront size
 // int5 rows (the low-nibble plane, then the bit-4 plane) are read as int4
 // chunks plus each chunk's 4 bytes of bit 4, in either form.
 //
-// Fast form (G == 16 and K % 256 == 0: every shape of the decoder): a lane owns
-// J rows and holds S of its chunks per row in registers at a time; the row is
-// walked in CPL/S segments of S chunks (S divides CPL). General form (any K %
-// 32 == 0): one row per lane, one chunk at a time.
+// Fast form (G == 16, K % 256 == 0 and an even CPL: every shape of the
+// decoder): a lane owns J rows and holds S = 2 of its chunks per row in
+// registers at a time; the row is walked in CPL/2 segments. General form (any
+// K % 32 == 0): one row per lane, one chunk at a time.
+//
+// This kernel serves M <= 2 activation rows (the matrix-core kernel takes
+// 3 <= M <= 16).
 constexpr int kGemvThreads = 256;   // 4 wavefronts per workgroup
 constexpr int kGemvWaves = kGemvThreads / kWave;
-constexpr int kGemvMaxMT = 4;       // activation rows per pass over the codes
+constexpr int kGemvMaxMT = 2;       // activation rows of the fp32-FMA kernel
 constexpr int kGemvGenBlocks = 96;  // blocks of x staged per segment in the general form
 constexpr int kNonTemporal = 2;     // cache policy of the weight loads: streamed once
 
-enum GemvKind { kGemvJ2S2 = 0, kGemvJ1S2, kGemvJ1S4, kGemvJ1S6, kGemvJ1S8, kGemvGeneral };
+enum GemvKind { kGemvJ4S2 = 0, kGemvJ1S2, kGemvGeneral };
 
 struct GemvGeom {
     int G;           // lanes per row
@@ -46,15 +49,14 @@ struct GemvGeom {
     int nb;          // blocks of x (and, fast form, of scales) staged per segment
 };
 
-// Single launches with few items use one row per lane to spread over the chip;
-// the grouped launch always uses the same shape for a given (K, bits, mt).
-// With one or two activation rows (mt <= 2) every fast shape with an even
-// chunk count per lane takes two rows per lane in segments of two chunks: each
-// staged x piece read from LDS then serves two weight rows (measured 4-5%
-// faster at M = 1 and 9% at M = 2 than one row per lane with longer segments).
-// J and S never change the arithmetic of an output (it depends on K and bits
-// only).
-__host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bool grouped, int mt = 1)
+// Fast shapes take four rows per lane, so each staged x piece read from LDS
+// serves four weight rows (measured 3-5% faster at M = 1 and 2 than two rows
+// per lane, and 9% faster at M = 2 than one row per lane with longer
+// segments); single launches with few items take one row per lane to spread
+// over the chip. J and S never change the arithmetic of an output (it depends
+// on K and bits only), so every shape and the grouped launch give the same
+// bits.
+__host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bool grouped)
 {
     GemvGeom g;
     const int cpb = bits / 4;
@@ -67,22 +69,12 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
     g.J = 1;
     g.S = 1;
     g.kind = kGemvGeneral;
-    if (G == 16 && K % 256 == 0) {
-        const int64_t rows_j2 = (int64_t)kGemvWaves * 4 * 2;
-        if (g.CPL == 2 || (mt <= 2 && g.CPL % 2 == 0)) {
-            const bool few = !grouped && (N + rows_j2 - 1) / rows_j2 < 256;
-            g.kind = few ? kGemvJ1S2 : kGemvJ2S2;
-            g.J = few ? 1 : 2;
-            g.S = 2;
-        } else if (bits != 8 && g.CPL % 6 == 0) {
-            g.kind = kGemvJ1S6; g.S = 6;
-        } else if (bits == 8 && g.CPL % 8 == 0) {
-            g.kind = kGemvJ1S8; g.S = 8;
-        } else if (g.CPL % 4 == 0) {
-            g.kind = kGemvJ1S4; g.S = 4;
-        } else if (g.CPL % 2 == 0) {
-            g.kind = kGemvJ1S2; g.S = 2;
-        }
+    if (G == 16 && K % 256 == 0 && g.CPL % 2 == 0) {
+        const int64_t rows_j4 = (int64_t)kGemvWaves * 4 * 4;
+        const bool few = !grouped && (N + rows_j4 - 1) / rows_j4 < 256;
+        g.kind = few ? kGemvJ1S2 : kGemvJ4S2;
+        g.J = few ? 1 : 4;
+        g.S = 2;
     }
     g.rows = (int64_t)kGemvWaves * (kWave / G) * g.J;
     if (g.kind == kGemvGeneral) {
@@ -98,14 +90,12 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
 // consecutive weight rows of one tensor.
 constexpr int kMgemvRows = 128;
 constexpr int kMgemvMinM = 3;
-
-// Activation rows staged at once (m-group size): 1, 2 or 4.
-__host__ __device__ inline int gemv_mt(int64_t M) { return M <= 2 ? (int)M : kGemvMaxMT; }
+static_assert(kMgemvMinM == kGemvMaxMT + 1, "every M has one decode kernel");
 
 // Rows per work item of a decode call with M activation rows.
 __host__ __device__ inline int64_t decode_item_rows(int64_t K, int bits, int64_t N, bool grouped, int64_t M)
 {
-    return M >= kMgemvMinM ? (int64_t)kMgemvRows : gemv_geom(K, bits, N, grouped, gemv_mt(M)).rows;
+    return M >= kMgemvMinM ? (int64_t)kMgemvRows : gemv_geom(K, bits, N, grouped).rows;
 }
 
 // LDS of an item: MT staged x rows (128 bytes per block) and, in the fast form,
