@@ -497,8 +497,13 @@ __device__ __forceinline__ void grouped_item(const wq_desc &d, int M, const uint
     const GemvGeom g = gemv_geom(K, BITS, d.N, true);
     const int64_t row0 = item * g.rows;
     // the shapes gemv_geom gives a grouped launch
-    if (g.kind == kGemvJ4S2) gemv_item_fast<BITS, MT, 4, 2>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
-    else gemv_item_general<BITS, MT>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
+    if constexpr (BITS == 5) {
+        if (g.kind == kGemvJ2S2) gemv_item_fast<BITS, MT, 2, 2>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+        else gemv_item_general<BITS, MT>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
+    } else {
+        if (g.kind == kGemvJ4S2) gemv_item_fast<BITS, MT, 4, 2>(d.x, M, K, d.N, q, s, d.y, row0, g.CPL, lds);
+        else gemv_item_general<BITS, MT>(d.x, M, K, d.N, q, s, d.y, row0, g, lds);
+    }
 }
 
 // Wavefronts per SIMD the grouped kernel is compiled for: the kernel holds every
@@ -542,7 +547,8 @@ hipError_t launch_gemv_mt(const float *x, int64_t M, int64_t K, int64_t N, const
 {
     const GemvGeom g = gemv_geom(K, BITS, N, false);
     switch (g.kind) {
-    case kGemvJ4S2: return launch_kind<BITS, MT, 4, 2>(x, M, K, N, q, s, y, g, stream);
+    case kGemvJ4S2: return launch_kind<BITS, MT, BITS == 5 ? 2 : 4, 2>(x, M, K, N, q, s, y, g, stream);
+    case kGemvJ2S2: return launch_kind<BITS, MT, 2, 2>(x, M, K, N, q, s, y, g, stream);
     case kGemvJ1S2: return launch_kind<BITS, MT, 1, 2>(x, M, K, N, q, s, y, g, stream);
     default: return launch_kind<BITS, MT, 1, 0>(x, M, K, N, q, s, y, g, stream);
     }

@@ -37,7 +37,7 @@ constexpr int kGemvMaxMT = 2;       // activation rows of the fp32-FMA kernel
 constexpr int kGemvGenBlocks = 96;  // blocks of x staged per segment in the general form
 constexpr int kNonTemporal = 2;     // cache policy of the weight loads: streamed once
 
-enum GemvKind { kGemvJ4S2 = 0, kGemvJ1S2, kGemvGeneral };
+enum GemvKind { kGemvJ4S2 = 0, kGemvJ2S2, kGemvJ1S2, kGemvGeneral };
 
 struct GemvGeom {
     int G;           // lanes per row
@@ -70,10 +70,12 @@ __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int bits, int64_t N, bo
     g.S = 1;
     g.kind = kGemvGeneral;
     if (G == 16 && K % 256 == 0 && g.CPL % 2 == 0) {
-        const int64_t rows_j4 = (int64_t)kGemvWaves * 4 * 4;
-        const bool few = !grouped && (N + rows_j4 - 1) / rows_j4 < 256;
-        g.kind = few ? kGemvJ1S2 : kGemvJ4S2;
-        g.J = few ? 1 : 4;
+        // int5 holds a bit-4 dword per chunk besides the codes: two rows per lane
+        const int jf = bits == 5 ? 2 : 4;
+        const int64_t rows_f = (int64_t)kGemvWaves * 4 * jf;
+        const bool few = !grouped && (N + rows_f - 1) / rows_f < 256;
+        g.kind = few ? kGemvJ1S2 : (jf == 4 ? kGemvJ4S2 : kGemvJ2S2);
+        g.J = few ? 1 : jf;
         g.S = 2;
     }
     g.rows = (int64_t)kGemvWaves * (kWave / G) * g.J;
