@@ -200,6 +200,24 @@ def test_gemm_parity(torch, bits, K, N):
                 assert np.linalg.norm(y[m] - y_ref[m]) <= 2e-3 * den, m
 
 
+@pytest.mark.parametrize("bits", [4, 5, 8])
+def test_gemm_tall_tiles(torch, bits):
+    """M >= 256 with at least 256 tiles of 128 x 128 takes 128-row tiles; ragged
+    M (2100 = 16 tiles + 52 rows), N (2000 = 15 tiles + 80 columns) and K (three
+    blocks: the last K stage is half past K)."""
+    M, K, N = 2100, 128 if bits == 5 else 96, 2000
+    w = _weights(N, K, (14, bits))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    x = inputs.normal((M, K), seed=(15, bits))
+    x[::97] *= 20
+    y_ref, _ = oracle.matmul(x, q_ref, s_ref, bits)
+    y16, B16 = oracle.matmul(x, q_ref, s_ref, bits, x16=True)
+    note(f"gemm tall tiles bits={bits} M={M} K={K} N={N}")
+    y = to_host(wqa.gemm(to_dev(x), to_dev(q_ref), to_dev(s_ref), bits))
+    check_gemm(y, y_ref, f"gemm tall bits={bits}")
+    check_gemv(y, y16, B16, f"gemm tall vs x16 bits={bits}")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_gemm_one_hot_and_selection(torch, bits):
     K, N = 96, 150

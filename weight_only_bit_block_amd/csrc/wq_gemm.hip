@@ -4,11 +4,12 @@
 // prefill GEMM that unpacks each weight group once and reuses it across all
 // activation rows. On gfx950 (wave64, fp16 matrix cores, 160 KiB LDS):
 //
-//  * A group of 4 wavefronts computes a BM x 128 tile of y (BM = 64, or 32 for
-//    small problems); wavefront w owns 32 output columns and all BM rows (BM/32
-//    fragments of 32 x 32), so each weight code of the tile is unpacked exactly
-//    once, in the registers of the wavefront that uses it, into an exact
-//    binary16 integer, and that unpack feeds every row fragment.
+//  * A group of 4 wavefronts computes a BM x 128 tile of y (BM = 128 for long
+//    prefills, 64, or 32 for small problems); wavefront w owns 32 output
+//    columns and all BM rows (BM/32 fragments of 32 x 32), so each weight code
+//    of the tile is unpacked exactly once, in the registers of the wavefront
+//    that uses it, into an exact binary16 integer, and that unpack feeds every
+//    row fragment.
 //  * When there are too few tiles to occupy the chip, a workgroup holds S = 2
 //    or 4 such groups that split the tile's K loop; groups 1..S-1 hand their
 //    fp32 sums to group 0 through LDS, which adds them in group order, so the
@@ -22,11 +23,10 @@
 //  * Each block of 32 values is two chained v_mfma_f32_32x32x16_f16 per 32 x 32
 //    fragment from a zero accumulator: the block's fp32 partial, which is then
 //    scaled by the block scale of its column and added to the fp32 accumulator
-//    (one fused multiply-add per output and block). The scaling of block k-1 is
-//    issued after the matrix instructions of block k, across stage boundaries,
-//    so vector and matrix work of one wavefront overlap. The 32x32x16 shape is
-//    used rather than 16x16x32 because on gfx950 it sustains twice the fp16
-//    matrix throughput per instruction issued.
+//    (one fused multiply-add per output and block), while the matrix work of
+//    the compute unit's other wavefronts runs. The 32x32x16 shape is used
+//    rather than 16x16x32 because on gfx950 it sustains twice the fp16 matrix
+//    throughput per instruction issued.
 //  * Within a block the 32 values are visited in the order the unpack produces
 //    them, identically for x and the weights, so each dot product is unchanged.
 //  * Tiles are ordered so that the workgroups placed on one XCD (workgroup id
@@ -49,7 +49,7 @@ constexpr int KT = 2;              // quantization blocks per stage
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
-// LDS layout of one stage buffer (BM rows per workgroup tile; 64 as launched).
+// LDS layout of one stage buffer (BM rows per workgroup tile: 32, 64 or 128).
 //   A: x as binary16, [BM rows][KT*32 values]; row pitch 128 bytes, 16-byte
 //      slot s of row r stored at slot s ^ ((r >> 1) & 7).
 //   B: packed codes, [BN columns][KT * CB bytes] (int5: the low nibbles).
@@ -214,20 +214,6 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     const f16v zero = {};
     const int c = wave * 32 + (lane & 31);       // this lane's column of the tile
     const int g = lane >> 5;                     // its k-group within a K-step of 16
-    // Blocks are pipelined: the matrix work of block k is issued, then the partials
-    // of block k-1 are scaled while it runs (also across stage boundaries).
-    f16v pp[RF];                                 // partials of the previous block
-    float scp = 0.0f;                            // and its scale (0 before the first block)
-#pragma unroll
-    for (int i = 0; i < RF; ++i) pp[i] = zero;
-    auto scale_prev = [&]() {
-#pragma unroll
-        for (int i = 0; i < RF; ++i) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][v] = __builtin_fmaf(scp, pp[i][v], acc[i][v]);
-            asm volatile("" : "+v"(acc[i]));    // the scaling happens here
-        }
-    };
     for (int it = 0; it < NTh; ++it) {
         const int cur = it & 1;
         const uint8_t *base = lds + cur * L::BYTES;
@@ -267,10 +253,14 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
                 const h8 a = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + 2 + g) * 16);
                 p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[1], p[i], 0, 0, 0);
             }
-            scale_prev();                            // acc += scale * partial of the previous block
+            // acc += scale * partial, block by block; the matrix work of other
+            // wavefronts runs meanwhile
 #pragma unroll
-            for (int i = 0; i < RF; ++i) pp[i] = p[i];
-            scp = sc;
+            for (int i = 0; i < RF; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][v] = __builtin_fmaf(sc, p[i][v], acc[i][v]);
+                asm volatile("" : "+v"(acc[i]));    // the scaling happens here
+            }
         }
         if (it + 1 < NTh) {
             commit(it + 1, cur ^ 1);             // waits for stage it+1's loads
@@ -278,8 +268,6 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
             if (it + 2 < NTh) issue(it + 2);
         }
     }
-    scale_prev();
-
     if constexpr (S > 1) {
         // groups 1..S-1 hand their partial sums to group 0 through LDS, which
         // adds them in group order (a fixed order: results are deterministic)
@@ -326,17 +314,19 @@ hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const vo
     return hipGetLastError();
 }
 
-// Tile height and K split. With at least 256 tiles of 64 x 128 (one or more
-// per CU), one group of 4 wavefronts per tile. Fewer: 32-row tiles with the K
-// loop of each tile split over 4 groups (2 when it has fewer than 4 stages), so
-// every SIMD runs several wavefronts; the time of a tile is then about a quarter
-// of its serial K loop.
+// Tile height and K split. With at least 256 tiles of 128 x 128 (M >= 256),
+// 128-row tiles: each unpacked code feeds four row fragments (measured 3-9%
+// faster than 64 rows at M = 4096). Else with at least 256 tiles of 64 x 128,
+// 64-row tiles; fewer: 32-row tiles with the K loop of each tile split over 4
+// groups (2 when it has fewer than 4 stages), so every SIMD runs several
+// wavefronts; the time of a tile is then about a quarter of its serial K loop.
 template <int BITS>
 hipError_t launch_shape(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                         const uint16_t *scales, float *y, hipStream_t stream)
 {
     const int64_t tn = (N + BN - 1) / BN;
     const int64_t stages = (K / 32 + KT - 1) / KT;
+    if (M >= 256 && ((M + 127) / 128) * tn >= 256) return launch_bits<BITS, 128, 1>(x, M, K, N, q, scales, y, stream);
     if (((M + 63) / 64) * tn >= 256 || stages < 2) return launch_bits<BITS, 64, 1>(x, M, K, N, q, scales, y, stream);
     if (stages < 4) return launch_bits<BITS, 32, 2>(x, M, K, N, q, scales, y, stream);
     return launch_bits<BITS, 32, 4>(x, M, K, N, q, scales, y, stream);
