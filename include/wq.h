@@ -145,7 +145,7 @@ int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits,
  * descriptors; a device copy of it drives wq_gemv_grouped.
  */
 typedef struct wq_desc {
-    int32_t bits;          /* 4 or 8 */
+    int32_t bits;          /* 4, 5 or 8 */
     int32_t reserved;      /* must be 0 */
     int64_t N;             /* output features (rows of q) */
     int64_t K;             /* input features, multiple of 32 */
