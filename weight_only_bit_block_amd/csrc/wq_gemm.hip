@@ -52,7 +52,8 @@ constexpr int kXcds = 8;
 // LDS layout of one stage buffer (BM rows per workgroup tile: 32, 64 or 128).
 //   A: x as binary16, [BM rows][KT*32 values]; row pitch 128 bytes, 16-byte
 //      slot s of row r stored at slot s ^ ((r >> 1) & 7).
-//   B: packed codes, [BN columns][KT * CB bytes] (int5: the low nibbles).
+//   B: packed codes, [BN columns][KT * CB bytes] (int5: the low nibbles), each
+//      column in 8-byte units rotated as CodeUnits describes.
 //   H: int5 only, bit 4 of the codes, [BN columns][KT dwords].
 //   S: binary16 scales, [BN columns][KT].
 template <int BITS, int BM>
@@ -66,6 +67,19 @@ struct Stage {
 };
 
 __device__ __forceinline__ int aslot(int r, int s) { return r * (KT * 4) + (s ^ ((r >> 1) & 7)); }
+
+// B holds column c's KT * CB code bytes in 8-byte units rotated by a
+// column-dependent amount, so that the code reads of a wavefront's 32 columns
+// (one unit index for all of them) hit distinct banks: unit u of column c is
+// stored at unit (u + rot(c)) % P.
+template <int CB>
+struct CodeUnits {
+    static constexpr int COLB = KT * CB;                 // bytes per column
+    static constexpr int P = COLB / 8;                   // units per column (4 or 8)
+    static constexpr int L = COLB == 32 ? 3 : 2;         // columns c, c + 2^L, ... share banks
+    __device__ static constexpr int rot(int c) { return (c >> L) & (P - 1); }
+    __device__ static constexpr int off(int c, int u) { return c * COLB + ((u + rot(c)) & (P - 1)) * 8; }
+};
 
 template <int BITS, int BM, int S>
 __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1)) void gemm_kernel(const float *__restrict__ x, int M, int K, int N,
@@ -177,7 +191,14 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     auto commit = [&](int st, int buf) {
         uint8_t *base = lds + buf * L::BYTES;
 #pragma unroll
-        for (int i = 0; i < QI; ++i) *reinterpret_cast<u4 *>(base + L::A_BYTES + (t + i * kThreads) * 16) = qv[i];
+        for (int i = 0; i < QI; ++i) {
+            // piece pc = 16-byte piece k of column c: units 2k and 2k + 1
+            using U = CodeUnits<CB>;
+            const int pc = t + i * kThreads;
+            const int cc = pc / (U::COLB / 16), k = pc - cc * (U::COLB / 16);
+            *reinterpret_cast<u2 *>(base + L::A_BYTES + U::off(cc, 2 * k)) = u2{qv[i].x, qv[i].y};
+            *reinterpret_cast<u2 *>(base + L::A_BYTES + U::off(cc, 2 * k + 1)) = u2{qv[i].z, qv[i].w};
+        }
 #pragma unroll
         for (int i = 0; i < XI; ++i) {
             const float v[8] = {xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w,
@@ -225,17 +246,18 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
             // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
             // unpacked once and used by every row fragment
             h8 b[2];
-            const uint8_t *qp = B + c * (KT * CB) + kb * CB;
+            using U = CodeUnits<CB>;
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 if constexpr (BITS == 4) {
-                    b[st] = unpack8_int4(*reinterpret_cast<const uint32_t *>(qp + (2 * st + g) * 4), dc);
+                    // dword 2*st + g of the block: unit 2*kb + st, dword g of it
+                    b[st] = unpack8_int4(*reinterpret_cast<const uint32_t *>(B + U::off(c, 2 * kb + st) + g * 4), dc);
                 } else if constexpr (BITS == 5) {
                     // bit 4 of these 8 codes: byte 2*st+g of the block's dword
                     const uint32_t hbyte = H[(c * KT + kb) * 4 + 2 * st + g];
-                    b[st] = unpack8_int5(*reinterpret_cast<const uint32_t *>(qp + (2 * st + g) * 4), hbyte, dc5);
+                    b[st] = unpack8_int5(*reinterpret_cast<const uint32_t *>(B + U::off(c, 2 * kb + st) + g * 4), hbyte, dc5);
                 } else {
-                    const u2 v = *reinterpret_cast<const u2 *>(qp + (2 * st + g) * 8);
+                    const u2 v = *reinterpret_cast<const u2 *>(B + U::off(c, 4 * kb + 2 * st + g));
                     b[st] = unpack8_int8(v.x, v.y, dc);
                 }
             }
