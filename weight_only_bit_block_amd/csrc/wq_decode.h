@@ -151,6 +151,56 @@ __device__ __forceinline__ h8 unpack8_int5(uint32_t d, uint32_t hbyte, const Dec
     return r;
 }
 
+// Codes straight to exact fp32 values with full-rate bit operations (no
+// binary16 step, no conversion): a code field c in offset form (c + 8 or
+// c + 128, by flipping its top bit) is placed in the mantissa of 2^23, which
+// gives the float 2^23 + (c + offset) * 2^p for a field at bit p, and one fp32
+// subtract of 2^23 + offset * 2^p leaves c * 2^p exactly. Fields at bit 0
+// ("lo") give the code itself; fields at bit 4 (int4) or 8 (int8) ("hi") give
+// 16 or 256 times the code, which the caller accumulates separately and
+// scales back by the same power of two.
+struct DecodeF32Consts {
+    uint32_t m4lo, m4hi, k4lo, k4hi;   // int4: nibble masks at bits 0 and 4, 2^23 magic with the sign flip
+    uint32_t m8lo, m8hi, k8lo, k8hi;   // int8: byte masks at bits 0 and 8
+    __device__ __forceinline__ static DecodeF32Consts make()
+    {
+        DecodeF32Consts c;
+        c.m4lo = vgpr(0x0000000Fu);
+        c.m4hi = vgpr(0x000000F0u);
+        c.k4lo = vgpr(0x4B000008u);
+        c.k4hi = vgpr(0x4B000080u);
+        c.m8lo = vgpr(0x000000FFu);
+        c.m8hi = vgpr(0x0000FF00u);
+        c.k8lo = vgpr(0x4B000080u);
+        c.k8hi = vgpr(0x4B008000u);
+        return c;
+    }
+};
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// int4 dword holding codes k0..k7: lo[i] = k(2i), hi[i] = 16 * k(2i+1), exact.
+__device__ __forceinline__ void decode_int4_f32(uint32_t d, const DecodeF32Consts &c, float (&lo)[4], float (&hi)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t e = d >> (8 * i);
+        lo[i] = as_f32(c.k4lo ^ (e & c.m4lo)) - 8388616.0f;   // 2^23 + 8
+        hi[i] = as_f32(c.k4hi ^ (e & c.m4hi)) - 8388736.0f;   // 2^23 + 128
+    }
+}
+
+// int8 dword holding codes k0..k3: lo[i] = k(2i), hi[i] = 256 * k(2i+1), exact.
+__device__ __forceinline__ void decode_int8_f32(uint32_t d, const DecodeF32Consts &c, float (&lo)[2], float (&hi)[2])
+{
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t e = d >> (16 * i);
+        lo[i] = as_f32(c.k8lo ^ (e & c.m8lo)) - 8388736.0f;   // 2^23 + 128
+        hi[i] = as_f32(c.k8hi ^ (e & c.m8hi)) - 8421376.0f;   // 2^23 + 32768
+    }
+}
+
 // Position of k (0..7) within an 8-group in the operand order above.
 template <int BITS>
 __device__ __forceinline__ constexpr int operand_slot(int k)

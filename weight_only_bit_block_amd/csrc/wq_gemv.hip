@@ -26,13 +26,15 @@
 //    128-bit reads of 16 lanes hit distinct banks.
 //  * int5 rows are read as int4 chunks of low nibbles plus, per chunk, the 4
 //    bytes of its codes' bit 4 (a second load from the row's bit-4 plane).
-//  * Unpack in registers without int->float conversions (wq_decode.h); the fp32
-//    FMA takes the binary16 code directly as an operand (v_fma_mix_f32), so each
+//  * Unpack in registers without int->float conversions (wq_decode.h): with
+//    one activation row the fp32 FMA takes the binary16 code directly as an
+//    operand (v_fma_mix_f32); with two, codes go straight to exact fp32 values
+//    by bit operations and the FMAs are plain v_fma_f32. Either way each
 //    product q*x is exact and is accumulated in fp32.
 //  * Per chunk: two partial chains over its codes, then acc += scale * partial
 //    in fp32; lanes of a row are reduced with a DPP butterfly, so every lane of
 //    the group holds the same bits. The arithmetic of an output depends only on
-//    (K, bits): not on J, the item, M or the launch (single tensor or
+//    (K, bits, M): not on J, the item or the launch (single tensor or
 //    grouped), so every launch gives bitwise identical results.
 //
 // Error: summation depth per output is 16 + 1 + CC/G + log2(G) (CC chunks per
@@ -150,11 +152,18 @@ __device__ __forceinline__ void stage_x(const float *__restrict__ x, int M, int 
 
 // The arithmetic of one chunk index for the J rows of a lane: codes w[j] (16
 // bytes of row j) times the staged x of the chunk's block (read once for all J
-// rows), into two partial chains per (j, m); then acc += scale * (p0 + p1).
-// Piece p of the block's x row m is at xp[p] + m * xstride.
+// rows), into two partial chains per (j, m); then acc += scale * partial.
+// Piece p of the block's x row m is at xp[p] + m * xstride. Two forms, by the
+// number of activation rows; both give exact products and fp32 sums:
+//  * one row (chunk_fma_h): codes as binary16, two per packed fp16 op, and one
+//    v_fma_mix_f32 per product, the fewest instructions per code;
+//  * two rows (chunk_fma_f): codes straight to fp32 with full-rate bit ops and
+//    one subtract (no conversion), then full-rate v_fma_f32 per product.
+// Measured on the decode step: the second form is 7% faster at M = 2 and 5%
+// slower at M = 1.
 template <int BITS, int MT, int J>
-__device__ __forceinline__ void chunk_fma(const u4 (&w)[J], const uint8_t *const (&xp)[8], int xstride,
-                                          const DecodeConsts &dc, const float (&sc)[J], float (&acc)[J][MT])
+__device__ __forceinline__ void chunk_fma_h(const u4 (&w)[J], const uint8_t *const (&xp)[8], int xstride,
+                                            const DecodeConsts &dc, const float (&sc)[J], float (&acc)[J][MT])
 {
     float p0[J][MT], p1[J][MT];
 #pragma unroll
@@ -222,6 +231,72 @@ __device__ __forceinline__ void chunk_fma(const u4 (&w)[J], const uint8_t *const
     for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[j][m] = __builtin_fmaf(sc[j], p0[j][m] + p1[j][m], acc[j][m]);
+}
+
+template <int BITS, int MT, int J>
+__device__ __forceinline__ void chunk_fma_f(const u4 (&w)[J], const uint8_t *const (&xp)[8], int xstride,
+                                            const DecodeF32Consts &dc, const float (&sc)[J], float (&acc)[J][MT])
+{
+    // plo: codes at even positions; phi: codes at odd positions, times 16 (int4)
+    // or 256 (int8) as decoded
+    float plo[J][MT], phi[J][MT];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) { plo[j][m] = 0.0f; phi[j][m] = 0.0f; }
+#pragma unroll
+    for (int h = 0; h < (BITS == 4 ? 4 : 2); ++h) {       // groups of 8 codes: x pieces 2h, 2h+1 of xp
+        f4 xa[MT], xb[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            xa[m] = *reinterpret_cast<const f4 *>(xp[2 * h] + m * xstride);
+            xb[m] = *reinterpret_cast<const f4 *>(xp[2 * h + 1] + m * xstride);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            // the 8 codes and their x values: c[0..7] with x in xa.xyzw, xb.xyzw
+            float lo[4], hi[4];
+            if (BITS == 4) {
+                decode_int4_f32(w[j][h], dc, lo, hi);        // lo: k0 k2 k4 k6; hi: 16 * (k1 k3 k5 k7)
+            } else {
+                float l0[2], h0[2], l1[2], h1[2];
+                decode_int8_f32(w[j][2 * h], dc, l0, h0);     // k0 k2 | 256 * (k1 k3)
+                decode_int8_f32(w[j][2 * h + 1], dc, l1, h1); // k4 k6 | 256 * (k5 k7)
+                lo[0] = l0[0]; lo[1] = l0[1]; lo[2] = l1[0]; lo[3] = l1[1];
+                hi[0] = h0[0]; hi[1] = h0[1]; hi[2] = h1[0]; hi[3] = h1[1];
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                plo[j][m] = __builtin_fmaf(lo[0], xa[m].x, plo[j][m]);
+                phi[j][m] = __builtin_fmaf(hi[0], xa[m].y, phi[j][m]);
+                plo[j][m] = __builtin_fmaf(lo[1], xa[m].z, plo[j][m]);
+                phi[j][m] = __builtin_fmaf(hi[1], xa[m].w, phi[j][m]);
+                plo[j][m] = __builtin_fmaf(lo[2], xb[m].x, plo[j][m]);
+                phi[j][m] = __builtin_fmaf(hi[2], xb[m].y, phi[j][m]);
+                plo[j][m] = __builtin_fmaf(lo[3], xb[m].z, plo[j][m]);
+                phi[j][m] = __builtin_fmaf(hi[3], xb[m].w, phi[j][m]);
+            }
+        }
+    }
+    constexpr float kHi = BITS == 4 ? 0.0625f : 0.00390625f;   // 1/16 or 1/256: exact
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[j][m] = __builtin_fmaf(sc[j], __builtin_fmaf(phi[j][m], kHi, plo[j][m]), acc[j][m]);
+}
+
+// Unpack constants of the chunk form for MT activation rows.
+template <int MT> struct ChunkConsts { using type = DecodeConsts; };
+template <> struct ChunkConsts<2> { using type = DecodeF32Consts; };
+
+template <int BITS, int MT, int J>
+__device__ __forceinline__ void chunk_fma(const u4 (&w)[J], const uint8_t *const (&xp)[8], int xstride,
+                                          const typename ChunkConsts<MT>::type &dc, const float (&sc)[J],
+                                          float (&acc)[J][MT])
+{
+    if constexpr (MT == 1) chunk_fma_h<BITS, MT, J>(w, xp, xstride, dc, sc, acc);
+    else chunk_fma_f<BITS, MT, J>(w, xp, xstride, dc, sc, acc);
 }
 
 // int5 chunk: the int4 arithmetic above with the codes decoded from the chunk's
@@ -329,7 +404,8 @@ __device__ __forceinline__ void gemv_item_fast(const float *__restrict__ x, int 
     const int C = K >> 5;
     const uint32_t qrow = (uint32_t)K * BITS / 8;     // bytes per row of codes
     const int nseg = CPL / S;
-    const DecodeConsts dc = DecodeConsts::make();
+    typename ChunkConsts<MT>::type dc;
+    if constexpr (BITS != 5) dc = ChunkConsts<MT>::type::make();
     Decode5Consts dc5;
     if constexpr (BITS == 5) dc5 = Decode5Consts::make();
     constexpr int NL = BITS == 5 ? 2 * J * S : J * S;   // loads per segment (int5: + bit-4 dwords)
@@ -432,7 +508,8 @@ __device__ __forceinline__ void gemv_item_general(const float *__restrict__ x, i
     const int CC = C * CPB;
     const uint32_t qrow = (uint32_t)K * BITS / 8;
     const uint32_t hoff = (uint32_t)K / 2;      // int5: offset of the bit-4 plane in a row
-    const DecodeConsts dc = DecodeConsts::make();
+    typename ChunkConsts<MT>::type dc;
+    if constexpr (BITS != 5) dc = ChunkConsts<MT>::type::make();
     Decode5Consts dc5;
     if constexpr (BITS == 5) dc5 = Decode5Consts::make();
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * qrow);
