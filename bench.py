@@ -19,7 +19,7 @@ Also reported: the roofline of the grouped GEMV kernel (algorithmic bytes per
 launch / the kernel's duration, from HIP events on its stream around the timed
 region, one launch per step), the CPU oracle timed on the host cores, and secondary
 legs: the sequential and fused (q|k|v, gate|up) forms of the step, tied-
-embedding lookups, batched decode of the mixed package at M=4 and 16, the int5
+embedding lookups, batched decode of the mixed package at M=1, 2, 4, 8 and 16, the int5
 step, and the prefill GEMM (M=4096 gate/up/down int4 + int8 lm_head on the
 last 64 rows) in TFLOP/s against the fp16 matrix-core peak. --decode-only
 runs the decode-step leg alone (the profile counter runs use it).
@@ -266,10 +266,10 @@ def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
 
 def mixed_leg(torch, wqa, inputs, np, oracle, steps, warmup):
     """Batched decode over the mixed package (attention int8, MLP int4, lm_head
-    int8), one grouped launch per step at M = 4 and 16 (M >= 3 runs on the
-    matrix cores)."""
+    int8), one grouped launch per step at M = 1, 2, 4, 8 and 16 (M <= 2 on the
+    fp32-FMA kernel, M >= 3 on the matrix cores)."""
     out = {}
-    for M in (4, 16):
+    for M in (1, 2, 4, 8, 16):
         wl = inputs.decode_step(M, mixed=True)
         pkgs, calls, ys, host_w, _ = build_decode(torch, wqa, wl, COPIES)
         launch_ms, wall_ms = time_grouped(torch, calls, steps, warmup)
@@ -528,7 +528,7 @@ def main() -> int:
     if not args.decode_only:
         log("shared-input fusion (113 GEMVs)")
         result["decode_step_fused"] = fused_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
-        log("mixed package, batched decode (M = 4, 16)")
+        log("mixed package, batched decode (M = 1, 2, 4, 8, 16)")
         result["decode_step_mixed"] = mixed_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
         log("int5 decode step and GEMM")
         result["int5"] = int5_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup)
