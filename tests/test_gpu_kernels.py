@@ -117,13 +117,41 @@ def test_gemv_one_hot_readout(torch, bits):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_one_hot_every_code(torch, bits, M):
+    """Every code value in every position of a packed word: x rows = e_k read out
+    column k of the dequantized weights bitwise, on the fp32-FMA path (M = 1:
+    binary16 codes; M = 2: codes decoded straight to fp32). K = 1024 takes the
+    fast item form; k runs over every position of three blocks (first, middle,
+    last), and rows 0..255 hold every byte value."""
+    K, N = 1024, 512
+    rng = inputs.generator((8, bits))
+    q_ref = rng.integers(0, 256, (N, K * bits // 8), dtype=np.uint8)
+    # rows 0..255 (int4: 0..15 repeated) hold every byte value in every byte position
+    for n in range(256):
+        q_ref[n, :] = np.uint8(n)
+    s_ref = np.float16(rng.uniform(1e-3, 2e-2, (N, K // 32))).view(np.uint16)
+    wh = oracle.dequant(q_ref, s_ref, K, bits)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    ks = [blk * 32 + i for blk in (0, 13, 31) for i in range(32)]
+    note(f"gemv one-hot every code bits={bits} M={M}")
+    for j in range(0, len(ks), M):
+        kk = ks[j:j + M]
+        x = np.zeros((M, K), dtype=np.float32)
+        x[np.arange(M), kk] = 1.0
+        y = to_host(wqa.gemv(to_dev(x), q, s, bits))
+        assert np.array_equal(y.astype(np.float64), wh[:, kk].T), kk
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M", [1, 2, 4])
 def test_gemv_extreme_codes_zero_scales_signs(torch, bits, M):
     """Codes -8 / -128 everywhere in a third of the rows, zero scales; power-of-two
     homogeneity and determinism bitwise on both decode paths. Sign symmetry is
-    bitwise on the fp32-FMA path (M = 1); the matrix-core path (M >= 3) sums in
-    the matrix unit, whose last-bit rounding need not be sign-symmetric, so there
-    it is held to the GEMV bound and reported."""
+    bitwise on the fp32-FMA path (M = 1 with binary16 codes, M = 2 with codes
+    decoded straight to fp32); the matrix-core path (M >= 3) sums in the matrix
+    unit, whose last-bit rounding need not be sign-symmetric, so there it is held
+    to the GEMV bound and reported."""
     K, N = 1024, 96
     nb = K // 32
     rng = inputs.generator((6, bits))
@@ -142,7 +170,7 @@ def test_gemv_extreme_codes_zero_scales_signs(torch, bits, M):
     yn = to_host(wqa.gemv(to_dev(-x), q, s, bits))
     y8 = to_host(wqa.gemv(to_dev(x * np.float32(8.0)), q, s, bits))
     y2 = to_host(wqa.gemv(to_dev(x), q, s, bits))
-    if M == 1:
+    if M <= 2:
         assert np.array_equal(yn, -y)
     else:
         diff = np.abs(yn.astype(np.float64) + y.astype(np.float64))
