@@ -314,13 +314,23 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
     // column l%32.
     const int n = n0 + c;
+    if (m0 + BM <= M && n0 + BN <= N) {
+        // a whole tile: no per-value bounds checks (no branches between the stores)
+        float *yp = y + (size_t)(m0 + 4 * g) * N + n;
 #pragma unroll
-    for (int i = 0; i < RF; ++i)
+        for (int i = 0; i < RF; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int m = m0 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-            if (m < M && n < N) __builtin_nontemporal_store(acc[i][v], y + (size_t)m * N + n);
-        }
+            for (int v = 0; v < 16; ++v)
+                __builtin_nontemporal_store(acc[i][v], yp + (size_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * N);
+    } else {
+#pragma unroll
+        for (int i = 0; i < RF; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+                if (m < M && n < N) __builtin_nontemporal_store(acc[i][v], y + (size_t)m * N + n);
+            }
+    }
 }
 
 template <int BITS, int BM, int S>
