@@ -241,6 +241,10 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
         const uint8_t *B = base + L::A_BYTES;
         const uint8_t *H = B + L::B_BYTES;
         const uint16_t *Sc = reinterpret_cast<const uint16_t *>(H + L::H_BYTES);
+        // A fragments one K-step ahead (K-step q of the stage is at slot 2q + g)
+        h8 acur[RF];
+#pragma unroll
+        for (int i = 0; i < RF; ++i) acur[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), g) * 16);
 #pragma unroll
         for (int kb = 0; kb < KT; ++kb) {
             // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
@@ -265,16 +269,17 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
             asm volatile("" : "+v"(sc));             // fp32 scale: plain FMAs
             // block partial of every row fragment: two chained K-steps of 16
             f16v p[RF];
+            h8 anx[RF];
 #pragma unroll
-            for (int i = 0; i < RF; ++i) {
-                const h8 a = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + g) * 16);
-                p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[0], zero, 0, 0, 0);
+            for (int i = 0; i < RF; ++i) anx[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + 2 + g) * 16);
+#pragma unroll
+            for (int i = 0; i < RF; ++i) p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[i], b[0], zero, 0, 0, 0);
+            if (kb + 1 < KT) {
+#pragma unroll
+                for (int i = 0; i < RF; ++i) acur[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), (kb + 1) * 4 + g) * 16);
             }
 #pragma unroll
-            for (int i = 0; i < RF; ++i) {
-                const h8 a = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + 2 + g) * 16);
-                p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[1], p[i], 0, 0, 0);
-            }
+            for (int i = 0; i < RF; ++i) p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(anx[i], b[1], p[i], 0, 0, 0);
             // acc += scale * partial, block by block; the matrix work of other
             // wavefronts runs meanwhile
 #pragma unroll
