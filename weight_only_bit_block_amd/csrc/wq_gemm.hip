@@ -245,27 +245,37 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
         h8 acur[RF];
 #pragma unroll
         for (int i = 0; i < RF; ++i) acur[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), g) * 16);
+        // the stage's code words and scales of this lane, read together at the
+        // stage start (one LDS wait for the whole stage)
+        using U = CodeUnits<CB>;
+        u2 cw[KT][2];
+        uint32_t hbs[KT][2];
+        uint16_t scb[KT];
+#pragma unroll
+        for (int kb = 0; kb < KT; ++kb) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                if constexpr (BITS == 8) {
+                    cw[kb][st] = *reinterpret_cast<const u2 *>(B + U::off(c, 4 * kb + 2 * st + g));
+                } else {
+                    cw[kb][st].x = *reinterpret_cast<const uint32_t *>(B + U::off(c, 2 * kb + st) + g * 4);
+                    if constexpr (BITS == 5) hbs[kb][st] = H[(c * KT + kb) * 4 + 2 * st + g];
+                }
+            }
+            scb[kb] = Sc[c * KT + kb];
+        }
 #pragma unroll
         for (int kb = 0; kb < KT; ++kb) {
             // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
             // unpacked once and used by every row fragment
             h8 b[2];
-            using U = CodeUnits<CB>;
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                if constexpr (BITS == 4) {
-                    // dword 2*st + g of the block: unit 2*kb + st, dword g of it
-                    b[st] = unpack8_int4(*reinterpret_cast<const uint32_t *>(B + U::off(c, 2 * kb + st) + g * 4), dc);
-                } else if constexpr (BITS == 5) {
-                    // bit 4 of these 8 codes: byte 2*st+g of the block's dword
-                    const uint32_t hbyte = H[(c * KT + kb) * 4 + 2 * st + g];
-                    b[st] = unpack8_int5(*reinterpret_cast<const uint32_t *>(B + U::off(c, 2 * kb + st) + g * 4), hbyte, dc5);
-                } else {
-                    const u2 v = *reinterpret_cast<const u2 *>(B + U::off(c, 4 * kb + 2 * st + g));
-                    b[st] = unpack8_int8(v.x, v.y, dc);
-                }
+                if constexpr (BITS == 4) b[st] = unpack8_int4(cw[kb][st].x, dc);
+                else if constexpr (BITS == 5) b[st] = unpack8_int5(cw[kb][st].x, hbs[kb][st], dc5);
+                else b[st] = unpack8_int8(cw[kb][st].x, cw[kb][st].y, dc);
             }
-            float sc = (float)__builtin_bit_cast(_Float16, Sc[c * KT + kb]);
+            float sc = (float)__builtin_bit_cast(_Float16, scb[kb]);
             asm volatile("" : "+v"(sc));             // fp32 scale: plain FMAs
             // block partial of every row fragment: two chained K-steps of 16
             f16v p[RF];
