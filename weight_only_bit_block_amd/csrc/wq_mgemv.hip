@@ -348,22 +348,40 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
             scn = load_scales<SB>(sr, rows, C, b0 + SB);
             stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, b0 + SB, wq, lane);
         }
+        // A operands and factors one block ahead of their matrix instructions
+        h8 na0[MF], na1[MF];
+        f4 nef[MF];
+#pragma unroll
+        for (int f = 0; f < MF; ++f) {
+            const uint8_t *op = buf + f * A::OP_BYTES;
+            na0[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, 2 * g));
+            na1[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, 2 * g + 1));
+            nef[f] = *reinterpret_cast<const f4 *>(E + 8 * f + 4 * g);
+        }
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
             const int b = b0 + j;
-            // this lane's x rows 8f + 4g .. 8f + 4g + 3: their factors of block j
+            h8 ca0[MF], ca1[MF];
             f4 ef[MF];
 #pragma unroll
-            for (int f = 0; f < MF; ++f) ef[f] = *reinterpret_cast<const f4 *>(E + j * 16 + 8 * f + 4 * g);
+            for (int f = 0; f < MF; ++f) { ca0[f] = na0[f]; ca1[f] = na1[f]; ef[f] = nef[f]; }
+            if (j + 1 < SB) {
+#pragma unroll
+                for (int f = 0; f < MF; ++f) {
+                    const uint8_t *op = buf + f * A::OP_BYTES;
+                    na0[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, (j + 1) * 4 + 2 * g));
+                    na1[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, (j + 1) * 4 + 2 * g + 1));
+                    nef[f] = *reinterpret_cast<const f4 *>(E + (j + 1) * 16 + 8 * f + 4 * g);
+                }
+            }
             h8 bw[2];
             lane_codes<BITS, SB>(lc, j, dc, dc5, bw);
             const uint16_t sbits = (uint16_t)(scv.w[j >> 1] >> (16 * (j & 1)));
             const float sc = b < C ? (float)__builtin_bit_cast(_Float16, sbits) : 0.0f;
 #pragma unroll
             for (int f = 0; f < MF; ++f) {
-                const uint8_t *op = buf + f * A::OP_BYTES;
-                const h8 a0 = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, j * 4 + 2 * g));
-                const h8 a1 = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, j * 4 + 2 * g + 1));
+                const h8 a0 = ca0[f];
+                const h8 a1 = ca1[f];
                 f16v p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bw[0], zero, 0, 0, 0);
                 p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bw[1], p, 0, 0, 0);
                 // value v < 4 of lane (n, g): operand row 4g + v, i.e. x row
