@@ -378,6 +378,37 @@ def prefill_leg(torch, wqa, inputs, steps, warmup):
     }
 
 
+def layer_prefill_leg(torch, wqa, inputs, steps, warmup):
+    """Prefill through the seven int4 projections of one layer (M = 128 and
+    1024): one grouped prefill launch over the layer's tensor table, against the
+    seven wq_gemm launches issued back to back."""
+    out = {}
+    for M in (128, 1024):
+        wl = inputs.prefill_layer(M)
+        specs = [(t.bits, t.N, t.K) for t in wl.tensors]
+        pkg = wqa.Package(specs)
+        for i, t in enumerate(wl.tensors):
+            pkg.pack_into(i, torch.from_numpy(wl.weight(t)).cuda())
+        xs = [torch.from_numpy(wl.x_for(t)).cuda() for t in wl.tensors]
+        ys = [torch.empty((M, t.N), dtype=torch.float32, device="cuda") for t in wl.tensors]
+        call = wqa.GroupedCall(pkg, xs, ys, M, prefill=True)
+        g_ms, _ = time_grouped(torch, [call], steps, warmup)
+
+        def seq():
+            for i, t in enumerate(wl.tensors):
+                wqa.gemm(xs[i], pkg.q(i), pkg.scales(i), t.bits, out=ys[i])
+
+        s_ms, _ = time_grouped(torch, [seq], steps, warmup)
+        flops = sum(2 * M * t.N * t.K for t in wl.tensors)
+        out[f"m{M}"] = {"grouped_ms": round(g_ms, 5), "grouped_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
+                        "sequential_ms": round(s_ms, 5),
+                        "sequential_tflops": round(flops / (s_ms * 1e-3) / 1e12, 2),
+                        "workgroups": call.total_tiles}
+    out["note"] = ("7 int4 projections (q, k, v, o, gate, up, down) of one layer, 1% outlier rows; "
+                   "grouped = wq_gemm_grouped, one launch; sequential = 7 wq_gemm launches; HIP events")
+    return out
+
+
 def time_grouped(torch, calls, steps, warmup):
     """A step is one grouped launch (the whole decode step), issued directly on
     the current stream as a decode loop issues it; the timed region runs `steps`
@@ -535,6 +566,9 @@ def main() -> int:
     if not args.no_prefill and not args.decode_only:
         log("prefill leg")
         result["prefill"] = prefill_leg(torch, wqa, inputs, max(3, args.steps // 10), max(1, args.warmup // 10))
+        log("layer prefill leg (grouped prefill launch)")
+        result["layer_prefill"] = layer_prefill_leg(torch, wqa, inputs, max(20, args.steps // 5),
+                                                    max(5, args.warmup // 5))
     if not args.no_cpu_baseline and not args.decode_only:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, oracle, np)

@@ -114,6 +114,8 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
  * one quantization block, computed by fp16 matrix-core instructions into an
  * fp32 partial that is then scaled by that block's scale.
  * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call.
+ * Sizes: M * K * 4 (the bytes of x), N * K * bits / 8 and N * K / 16 must each
+ * be below 2^32 (32-bit offsets in the kernel), else WQ_ERR_SHAPE.
  */
 int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
             const void *q, const uint16_t *scales, float *y, hipStream_t stream);
@@ -180,6 +182,33 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles);
  * The calls must be independent (no call reads another call's y).
  */
 int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
+                    int64_t total_tiles, int64_t M, hipStream_t stream);
+
+/*
+ * wq_table_plan_gemm -- host only. For a grouped prefill call (wq_gemm_grouped)
+ * with M >= 1 rows, set tile_begin of every entry and return the launch size in
+ * *total_tiles. Validates every entry as wq_table_plan does, and M * K * 4 <
+ * 2^32 for each. Work items are dispatched longest K first (ties in table
+ * order), and each entry's items start at a multiple of 8. The tile shape
+ * depends on M only, so a plan is valid for exactly the M it was made with.
+ */
+int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles);
+
+/*
+ * wq_gemm_grouped -- one launch that runs the prefill GEMM of every tensor in a
+ * planned table (the devpost page's blocked prefill GEMM, "How we built it",
+ * over all projections of a layer at once, so that short prefills fill the
+ * chip). `table_dev` is a device copy of a table planned by wq_table_plan_gemm
+ * with the same M; `base` is the package base (64-byte aligned). Each call's y
+ * [M][N] is computed as wq_gemm computes it (same unpack, binary16 rounding of
+ * x and per-block fp32 scaling), with one tile shape for the whole launch:
+ * 32-row tiles with each tile's K loop split four ways for M <= 128, 64-row tiles
+ * for M <= 512, 128-row tiles above. The result is deterministic and meets
+ * wq_gemm's error bound; it equals wq_gemm bitwise when both use the same tile
+ * shape. The calls must be independent (no call reads another call's y, and
+ * the y of different entries do not overlap).
+ */
+int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count,
                     int64_t total_tiles, int64_t M, hipStream_t stream);
 
 /* Human-readable text for a wq_status value (static storage). */

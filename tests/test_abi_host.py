@@ -24,10 +24,10 @@ def test_exports_every_header_symbol(lib):
     syms = W.header_symbols()
     assert {"wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_grouped",
             "wq_table_layout", "wq_table_plan", "wq_q_bytes", "wq_s_bytes", "wq_strerror",
-            "wq_embed", "wq_abi_version"} <= set(syms)
+            "wq_embed", "wq_abi_version", "wq_table_plan_gemm", "wq_gemm_grouped"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.wq_abi_version() == 3
+    assert lib.wq_abi_version() == 4
 
 
 def test_sizes(lib):
@@ -143,6 +143,82 @@ def test_grouped_validation(lib):
     assert lib.wq_gemv_grouped(FAKE + 16, FAKE, 3, 10, 1, None) == ALIGN
     assert lib.wq_gemv_grouped(FAKE, FAKE + 16, 3, 10, 1, None) == ALIGN
     assert lib.wq_gemv_grouped(None, None, 0, 0, 1, None) == OK
+
+
+def test_gemm_x_offset_limit(lib):
+    """The prefill kernels address x with 32-bit byte offsets: M * K * 4 >= 2^32
+    is refused before anything is launched."""
+    for fn in ("wq_gemm", "wq_linear"):
+        assert getattr(lib, fn)(FAKE, 1 << 20, 1024, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+
+
+def _gemm_items(M, N):
+    bm = 32 if M <= 128 else (64 if M <= 512 else 128)
+    return -(-M // bm) * -(-N // 128)
+
+
+@pytest.mark.parametrize("M", [1, 100, 128, 129, 512, 513, 1024, 4096])
+def test_table_plan_gemm(lib, M):
+    """Grouped prefill plan: longest K first (ties in table order), entries at
+    multiples of 8 items, one tile shape per M."""
+    specs = [(4, 2048, 1024), (4, 1024, 1024), (4, 1024, 2048), (8, 3, 96), (4, 1024, 3072),
+             (5, 300, 1024)]
+    arr, _ = wqa.table_layout(specs)
+    with pytest.raises(wqa.WqError):
+        wqa.table_plan_gemm(arr, M)                  # x / y not bound yet
+    for i in range(len(specs)):
+        arr[i].x, arr[i].y = FAKE, FAKE
+    total = wqa.table_plan_gemm(arr, M)
+    order = sorted(range(len(specs)), key=lambda i: (-specs[i][2], i))
+    cur = 0
+    for i in order:
+        cur = -(-cur // 8) * 8
+        assert arr[i].tile_begin == cur, (i, arr[i].tile_begin, cur)
+        cur += _gemm_items(M, specs[i][1])
+    assert total == cur
+
+
+def test_table_plan_gemm_validation(lib):
+    specs = [(4, 256, 1024), (8, 128, 64)]
+    arr, _ = wqa.table_layout(specs)
+    for i in range(len(specs)):
+        arr[i].x, arr[i].y = FAKE, FAKE
+    for M in (0, -1, (1 << 30) + 1):
+        with pytest.raises(wqa.WqError) as e:
+            wqa.table_plan_gemm(arr, M)
+        assert e.value.status == MRANGE
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan_gemm(arr, 1 << 20)            # M * K * 4 >= 2^32
+    assert e.value.status == SHAPE
+    arr[1].y = MIS
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan_gemm(arr, 64)
+    assert e.value.status == ALIGN
+    arr[1].y = FAKE
+    arr[0].bits = 6
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan_gemm(arr, 64)
+    assert e.value.status == BITS
+    arr[0].bits = 4
+    arr[0].reserved = 1
+    with pytest.raises(wqa.WqError) as e:
+        wqa.table_plan_gemm(arr, 64)
+    assert e.value.status == TABLE
+    arr[0].reserved = 0
+    assert wqa.table_plan_gemm(arr, 64) > 0
+    empty = (W.WqDesc * 0)()
+    assert wqa.table_plan_gemm(empty, 64) == 0
+
+
+def test_gemm_grouped_validation(lib):
+    assert lib.wq_gemm_grouped(FAKE, FAKE, 3, 10, 0, None) == MRANGE
+    assert lib.wq_gemm_grouped(FAKE, FAKE, 3, 10, (1 << 30) + 1, None) == MRANGE
+    assert lib.wq_gemm_grouped(FAKE, FAKE, -1, 10, 64, None) == SHAPE
+    assert lib.wq_gemm_grouped(FAKE, FAKE, 3, 1 << 31, 64, None) == SHAPE
+    assert lib.wq_gemm_grouped(None, FAKE, 3, 10, 64, None) == NULL
+    assert lib.wq_gemm_grouped(FAKE + 16, FAKE, 3, 10, 64, None) == ALIGN
+    assert lib.wq_gemm_grouped(FAKE, FAKE + 16, 3, 10, 64, None) == ALIGN
+    assert lib.wq_gemm_grouped(None, None, 0, 0, 64, None) == OK
 
 
 def test_strerror(lib):

@@ -169,6 +169,36 @@ def test_prefill_layer_full(torch, M):
         print(f"[info] prefill M={M} {t.name}: rel Frobenius {rel:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("M", [128, 1024])
+def test_prefill_layer_grouped_full(torch, M):
+    """The seven int4 projections of one layer in one grouped prefill launch, at
+    M=128 / 1024 with 1% outlier rows; sampled rows (every outlier row) and
+    columns against the oracle."""
+    wl = inputs.prefill_layer(M)
+    specs = [(t.bits, t.N, t.K) for t in wl.tensors]
+    pkg = wqa.Package(specs)
+    ws = []
+    for i, t in enumerate(wl.tensors):
+        w = wl.weight(t)
+        pkg.pack_into(i, to_dev(w))
+        ws.append(w)
+    xs = [to_dev(wl.x_for(t)) for t in wl.tensors]
+    ys = [torch.full((M, t.N), float("nan"), dtype=torch.float32, device="cuda") for t in wl.tensors]
+    call = wqa.GroupedCall(pkg, xs, ys, M, prefill=True)
+    note(f"grouped prefill layer M={M}: {call.total_tiles} workgroups")
+    call()
+    torch.cuda.synchronize()
+    for i, t in enumerate(wl.tensors):
+        x = wl.x_for(t)
+        y = to_host(ys[i])
+        assert not np.isnan(y).any(), t.name
+        outl = np.where(np.abs(x).max(axis=1) > 8)[0]
+        m_rows = np.unique(np.concatenate([_sample(M, 24, (80, M, inputs.PROJ_ID[t.proj])), outl]))
+        n_cols = _sample(t.N, 512, (81, M, inputs.PROJ_ID[t.proj]))
+        rel = _gemm_check(x, ws[i], 4, y, m_rows, n_cols, f"grouped prefill M={M} {t.name}")
+        print(f"[info] grouped prefill M={M} {t.name}: rel Frobenius {rel:.2e}", flush=True)
+
+
 def test_long_prefill_full(torch):
     """M=4096 gate/up/down (int4) and the int8 lm_head on the last 64 rows."""
     wl = inputs.long_prefill()

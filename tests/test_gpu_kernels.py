@@ -353,3 +353,71 @@ def test_grouped_matches_per_tensor(torch, M):
         assert np.array_equal(got, single), i
         y_ref, B = oracle.matmul(to_host(xs[i]), refs[i][0], refs[i][1], bits)
         check_gemv(got, y_ref, B, f"grouped tensor {i}")
+
+
+# ------------------------------------------------------------------ grouped prefill
+GROUPED_GEMM_SPECS = [(4, 2048, 1024), (8, 300, 1024), (4, 1024, 2048), (5, 130, 256), (4, 3, 96),
+                      (8, 0, 64), (4, 77, 160), (5, 1024, 128), (8, 129, 32)]
+
+
+@pytest.mark.parametrize("M", [1, 17, 100, 128, 130, 512, 600])
+def test_gemm_grouped_matches_oracle(torch, M):
+    """One grouped prefill launch over int4 / int5 / int8 tensors with ragged N
+    and short and long K, at M covering the three tile shapes (32 rows split four
+    ways, 64 rows, 128 rows) and their ragged tails; every output is written
+    (y starts as NaN) and meets the GEMM bound against the oracle."""
+    specs = GROUPED_GEMM_SPECS
+    pkg = wqa.Package(specs)
+    refs = []
+    for i, (bits, N, K) in enumerate(specs):
+        w = _weights(N, K, (40, i))
+        q_ref, s_ref = oracle.quantize(w, bits)
+        if N:
+            pkg.q(i).copy_(to_dev(q_ref))
+            pkg.scales(i).copy_(to_dev(s_ref))
+        refs.append((q_ref, s_ref))
+    xs = []
+    for i, (_, _, K) in enumerate(specs):
+        x = inputs.normal((M, K), seed=(41, i, M))
+        x[M // 2] *= 20
+        xs.append(to_dev(x))
+    ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for (_, N, _) in specs]
+    call = wqa.GroupedCall(pkg, xs, ys, M, prefill=True)
+    note(f"grouped gemm M={M} tiles={call.total_tiles}")
+    call()
+    torch.cuda.synchronize()
+    for i, (bits, N, K) in enumerate(specs):
+        if N == 0:
+            continue
+        got = to_host(ys[i])
+        x = to_host(xs[i])
+        y_ref, _ = oracle.matmul(x, refs[i][0], refs[i][1], bits)
+        y16, B16 = oracle.matmul(x, refs[i][0], refs[i][1], bits, x16=True)
+        check_gemm(got, y_ref, f"grouped gemm M={M} tensor {i}")
+        check_gemv(got, y16, B16, f"grouped gemm vs x16 M={M} tensor {i}")
+
+
+def test_gemm_grouped_bitwise_as_single(torch):
+    """With the same tile shape (M <= 128, K >= 224 and few tiles: 32-row tiles,
+    K split four ways, in both paths) the grouped launch equals wq_gemm bitwise;
+    the same table run twice gives the same bits."""
+    M = 100
+    specs = [(4, 1000, 256), (8, 256, 512), (5, 300, 256), (4, 129, 1024)]
+    pkg = wqa.Package(specs)
+    for i, (bits, N, K) in enumerate(specs):
+        q_ref, s_ref = oracle.quantize(_weights(N, K, (42, i)), bits)
+        pkg.q(i).copy_(to_dev(q_ref))
+        pkg.scales(i).copy_(to_dev(s_ref))
+    xs = [to_dev(inputs.normal((M, K), seed=(43, i))) for i, (_, _, K) in enumerate(specs)]
+    ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for (_, N, _) in specs]
+    call = wqa.GroupedCall(pkg, xs, ys, M, prefill=True)
+    note(f"grouped gemm bitwise M={M} tiles={call.total_tiles}")
+    call()
+    torch.cuda.synchronize()
+    first = [to_host(y) for y in ys]
+    call()
+    torch.cuda.synchronize()
+    for i, (bits, N, K) in enumerate(specs):
+        single = to_host(wqa.gemm(xs[i], pkg.q(i), pkg.scales(i), bits))
+        assert np.array_equal(first[i], single), i
+        assert np.array_equal(to_host(ys[i]), first[i]), i

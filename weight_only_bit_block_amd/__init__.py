@@ -15,7 +15,7 @@ The library is loaded on first use and must have been built
 (``python -m weight_only_bit_block_amd.build``); there is no fallback.
 """
 from .wq import (BLOCK, GEMV_MAX_M, GroupedCall, Package, WqError, embed, gemm, gemv,
-                 header_symbols, linear, load, pack, table_layout, table_plan, unpack)
+                 header_symbols, linear, load, pack, table_layout, table_plan, table_plan_gemm, unpack)
 
 __all__ = ["BLOCK", "GEMV_MAX_M", "GroupedCall", "Package", "WqError", "embed", "gemm", "gemv",
-           "header_symbols", "linear", "load", "pack", "table_layout", "table_plan", "unpack"]
+           "header_symbols", "linear", "load", "pack", "table_layout", "table_plan", "table_plan_gemm", "unpack"]

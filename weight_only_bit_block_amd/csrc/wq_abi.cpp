@@ -1,5 +1,5 @@
 // wq_abi.cpp -- the C ABI: host-side validation, dispatch by M, planning of the
-// grouped decode launch and the 64-byte-aligned tensor table.
+// grouped decode and prefill launches and the 64-byte-aligned tensor table.
 //
 // Every check runs on the host before anything is launched; a failing check
 // returns a status and touches no HIP state. Launches go to the caller's
@@ -59,11 +59,37 @@ inline int gemv_offsets_ok(int64_t K, int64_t N, int bits)
     return WQ_OK;
 }
 
+// The prefill kernels address x (fp32, M x K) with 32-bit byte offsets.
+inline bool gemm_x_ok(int64_t M, int64_t K) { return (uint64_t)M * (uint64_t)K * 4 < ((uint64_t)1 << 32); }
+
 int gemm_grid_ok(int64_t M, int64_t N)
 {
     // the prefill tile is 64 x 128; the grid is rounded up to a multiple of 8
     const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
     return tiles <= (int64_t)0x7FFFFFF0 ? WQ_OK : WQ_ERR_SHAPE;
+}
+
+// Checks of one tensor-table entry of a grouped call with M rows.
+int check_entry(const wq_desc &d, int64_t M)
+{
+    int st = check_bits(d.bits);
+    if (st) return st;
+    st = check_shape(M, d.K, d.N);
+    if (st) return st;
+    st = check_row(d.K, d.bits);
+    if (st) return st;
+    st = gemv_offsets_ok(d.K, d.N, d.bits);
+    if (st) return st;
+    if (d.reserved != 0) return WQ_ERR_TABLE;
+    if ((d.q_off % WQ_TABLE_ALIGN) || (d.s_off % WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
+    if (d.s_off < d.q_off + (uint64_t)d.N * (uint64_t)d.K * (uint64_t)d.bits / 8 &&
+        d.q_off < d.s_off + (uint64_t)d.N * (uint64_t)(d.K / WQ_BLOCK) * 2 && d.N > 0)
+        return WQ_ERR_TABLE;                    // codes and scales overlap
+    if (d.N > 0) {
+        if (!d.x || !d.y) return WQ_ERR_NULL;
+        if (!aligned(d.x, 16) || !aligned(d.y, 16)) return WQ_ERR_ALIGN;
+    }
+    return WQ_OK;
 }
 
 }  // namespace
@@ -134,9 +160,9 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     if (empty) return WQ_OK;
     st = gemm_grid_ok(M, N);
     if (st) return st;
-    // the prefill kernel addresses codes and activations with 32-bit offsets
-    if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= ((uint64_t)1 << 32) ||
-        (uint64_t)M * (uint64_t)K >= ((uint64_t)1 << 32) || (uint64_t)N * (uint64_t)(K / WQ_BLOCK) >= ((uint64_t)1 << 32))
+    // the prefill kernel addresses codes, scales and x (fp32) with 32-bit byte offsets
+    if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= ((uint64_t)1 << 32) || !gemm_x_ok(M, K) ||
+        (uint64_t)N * (uint64_t)(K / WQ_BLOCK) * 2 >= ((uint64_t)1 << 32))
         return WQ_ERR_SHAPE;
     return hip_status(wq::launch_gemm(x, M, K, N, bits, q, scales, y, stream));
 }
@@ -198,23 +224,8 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
     int64_t cur = 0;
     for (int i = 0; i < count; ++i) {
         wq_desc &d = table[i];
-        int st = check_bits(d.bits);
+        const int st = check_entry(d, M);
         if (st) return st;
-        st = check_shape(M, d.K, d.N);
-        if (st) return st;
-        st = check_row(d.K, d.bits);
-        if (st) return st;
-        st = gemv_offsets_ok(d.K, d.N, d.bits);
-        if (st) return st;
-        if (d.reserved != 0) return WQ_ERR_TABLE;
-        if ((d.q_off % WQ_TABLE_ALIGN) || (d.s_off % WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
-        if (d.s_off < d.q_off + (uint64_t)d.N * (uint64_t)d.K * (uint64_t)d.bits / 8 &&
-            d.q_off < d.s_off + (uint64_t)d.N * (uint64_t)(d.K / WQ_BLOCK) * 2 && d.N > 0)
-            return WQ_ERR_TABLE;                // codes and scales overlap
-        if (d.N > 0) {
-            if (!d.x || !d.y) return WQ_ERR_NULL;
-            if (!aligned(d.x, 16) || !aligned(d.y, 16)) return WQ_ERR_ALIGN;
-        }
         d.tile_begin = cur;
         const int64_t rows = wq::decode_item_rows(d.K, d.bits, d.N, true, M);
         cur += (d.N + rows - 1) / rows;
@@ -236,6 +247,49 @@ int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count, int64
     return hip_status(wq::launch_gemv_grouped(base, table_dev, count, total_tiles, M, stream));
 }
 
+int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
+{
+    if (count < 0) return WQ_ERR_SHAPE;
+    if (!total_tiles || (count > 0 && !table)) return WQ_ERR_NULL;
+    if (M < 1 || M > kMaxDim) return WQ_ERR_M_RANGE;
+    for (int i = 0; i < count; ++i) {
+        const int st = check_entry(table[i], M);
+        if (st) return st;
+        if (!gemm_x_ok(M, table[i].K)) return WQ_ERR_SHAPE;
+    }
+    // dispatch order: longest K first (the longest K loops start first), ties in
+    // table order; each entry starts at a multiple of 8 work items
+    int64_t cur = 0, prev = INT64_MAX;
+    for (;;) {
+        int64_t k = -1;                         // the longest K below prev
+        for (int i = 0; i < count; ++i)
+            if (table[i].K < prev && table[i].K > k) k = table[i].K;
+        if (k < 0) break;
+        for (int i = 0; i < count; ++i) {
+            wq_desc &d = table[i];
+            if (d.K != k) continue;
+            cur = (cur + wq::kGemmGroupAlign - 1) / wq::kGemmGroupAlign * wq::kGemmGroupAlign;
+            d.tile_begin = cur;
+            cur += wq::gemm_grouped_items(M, d.N);
+            if (cur > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
+        }
+        prev = k;
+    }
+    *total_tiles = cur;
+    return WQ_OK;
+}
+
+int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_tiles,
+                    int64_t M, hipStream_t stream)
+{
+    if (M < 1 || M > kMaxDim) return WQ_ERR_M_RANGE;
+    if (count < 0 || total_tiles < 0 || total_tiles > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
+    if (count == 0 || total_tiles == 0) return WQ_OK;
+    if (!base || !table_dev) return WQ_ERR_NULL;
+    if (!aligned(base, WQ_TABLE_ALIGN) || !aligned(table_dev, WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
+    return hip_status(wq::launch_gemm_grouped(base, table_dev, count, total_tiles, M, stream));
+}
+
 const char *wq_strerror(int status)
 {
     switch (status) {
@@ -251,6 +305,6 @@ const char *wq_strerror(int status)
     }
 }
 
-int wq_abi_version(void) { return 3; }
+int wq_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -81,11 +81,21 @@ struct CodeUnits {
     __device__ static constexpr int off(int c, int u) { return c * COLB + ((u + rot(c)) & (P - 1)) * 8; }
 };
 
-template <int BITS, int BM, int S>
-__global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1)) void gemm_kernel(const float *__restrict__ x, int M, int K, int N,
-                                                           const uint8_t *__restrict__ q,
-                                                           const uint16_t *__restrict__ s,
-                                                           float *__restrict__ y, int tiles_m, int tiles_n)
+// Launch bounds of a workgroup of S groups: one 256-thread group (two
+// workgroups per compute unit) or S groups of 256 threads.
+#define WQ_GEMM_BOUNDS(S) __launch_bounds__(((S) == 1 ? kThreads : kThreads * (S)), ((S) == 1 ? 2 : 1))
+
+// Stages whose loads are in flight while one is computed: 2 for 32-row tiles
+// (short prefills, where a stage's few matrix instructions cannot cover a
+// memory round trip), else 1 (registers are needed for the row fragments).
+constexpr int gemm_prefetch(int BM) { return BM == 32 ? 2 : 1; }
+
+// One BM x 128 output tile (tm, tn) of y = x W^T; every thread of the
+// workgroup calls it. lds_all holds at least S * 2 * Stage<BITS, BM>::BYTES.
+template <int BITS, int BM, int S, int PF = gemm_prefetch(BM)>
+__device__ __forceinline__ void gemm_tile(const float *__restrict__ x, int M, int K, int N,
+                                          const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
+                                          float *__restrict__ y, int tm, int tn, uint8_t *lds_all)
 {
     using L = Stage<BITS, BM>;
     constexpr int CB = L::CB;
@@ -97,16 +107,6 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     // S groups of 4 wavefronts split the K loop; each group has its own two stage
     // buffers, and the partial sums of groups 1..S-1 are reduced through them.
     static_assert((S - 1) * kThreads * RF * 16 * 4 <= S * 2 * L::BYTES, "reduction fits the stage buffers");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_all[S * 2 * L::BYTES];
-
-    // XCD-aware tile order: workgroups id, id+8, id+16, ... run on one XCD; give
-    // them consecutive tiles (row-major over (tm, tn)).
-    const int T = tiles_m * tiles_n;
-    const int per = (T + kXcds - 1) / kXcds;
-    const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    if (tile >= T) return;
-    const int tm = tile / tiles_n;
-    const int tn = tile - tm * tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int t = threadIdx.x & (kThreads - 1);  // index within the K group
@@ -158,12 +158,22 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
         qoff[i] = (uint32_t)n * qrow + (uint32_t)((k * 16) % CB);
         qblk[i] = (k * 16) / CB;
     }
-    f4 xv[XI][2];
-    u4 qv[QI];
-    uint16_t sv[KT];
-    uint32_t hv[KT];                              // int5: bit-4 dwords of column sn
+    // one stage's loads in registers; PF sets in flight
+    struct Regs {
+        f4 xv[XI][2];
+        u4 qv[QI];
+        uint16_t sv[KT];
+        uint32_t hv[KT];                          // int5: bit-4 dwords of column sn
+    };
+    Regs rs[PF];
     const uint32_t hoff = (uint32_t)sn * qrow + (uint32_t)K / 2;
-    auto issue = [&](int st) {
+    // loads of stage st (every address clamped into the tensors, so a stage
+    // past the group's K range loads valid data that is never committed)
+    auto issue = [&](int st, Regs &r) {
+        auto &qv = r.qv;
+        auto &xv = r.xv;
+        auto &sv = r.sv;
+        auto &hv = r.hv;
         const int b0 = (st0 + st) * KT;
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
@@ -188,7 +198,11 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
     };
     // x rounded to binary16 in operand order, the codes and the scales (zero past
     // K), into buffer buf
-    auto commit = [&](int st, int buf) {
+    auto commit = [&](int st, int buf, const Regs &r) {
+        const auto &qv = r.qv;
+        const auto &xv = r.xv;
+        const auto &sv = r.sv;
+        const auto &hv = r.hv;
         uint8_t *base = lds + buf * L::BYTES;
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
@@ -227,15 +241,11 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
-    issue(0);
-    commit(0, 0);                                // waits for stage 0's loads
-    __syncthreads();
-    if (NTh > 1) issue(1);
-
     const f16v zero = {};
     const int c = wave * 32 + (lane & 31);       // this lane's column of the tile
     const int g = lane >> 5;                     // its k-group within a K-step of 16
-    for (int it = 0; it < NTh; ++it) {
+    // the matrix work of stage it, from LDS buffer it & 1
+    auto compute = [&](int it) {
         const int cur = it & 1;
         const uint8_t *base = lds + cur * L::BYTES;
         const uint8_t *B = base + L::A_BYTES;
@@ -299,11 +309,44 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
                 asm volatile("" : "+v"(acc[i]));    // the scaling happens here
             }
         }
-        if (it + 1 < NTh) {
-            commit(it + 1, cur ^ 1);             // waits for stage it+1's loads
-            __syncthreads();                     // every wave is done with buffer cur
-            if (it + 2 < NTh) issue(it + 2);
+    };
+
+    if constexpr (PF == 1) {
+        issue(0, rs[0]);
+        commit(0, 0, rs[0]);                     // waits for stage 0's loads
+        __syncthreads();
+        if (NTh > 1) issue(1, rs[0]);
+        for (int it = 0; it < NTh; ++it) {
+            compute(it);
+            if (it + 1 < NTh) {
+                commit(it + 1, (it + 1) & 1, rs[0]);   // waits for stage it+1's loads
+                __syncthreads();                 // every wave is done with buffer it & 1
+                if (it + 2 < NTh) issue(it + 2, rs[0]);
+            }
         }
+    } else {
+        // stage j's loads go to register set j % 2, issued two stages ahead, always
+        // (no load under a branch, so each commit waits only for its own set)
+        static_assert(PF == 2, "prefetch depth 1 or 2");
+        issue(0, rs[0]);
+        issue(1, rs[1]);
+        commit(0, 0, rs[0]);                     // waits for stage 0's loads only
+        __syncthreads();
+        issue(2, rs[0]);
+        int it = 0;
+        for (; it + 1 < NTh; it += 2) {
+            compute(it);
+            commit(it + 1, 1, rs[1]);
+            __syncthreads();
+            issue(it + 3, rs[1]);
+            compute(it + 1);
+            if (it + 2 < NTh) {
+                commit(it + 2, 0, rs[0]);
+                __syncthreads();
+            }
+            issue(it + 4, rs[0]);
+        }
+        if (it < NTh) compute(it);
     }
     if constexpr (S > 1) {
         // groups 1..S-1 hand their partial sums to group 0 through LDS, which
@@ -349,6 +392,54 @@ __global__ __launch_bounds__((S == 1 ? kThreads : kThreads * S), (S == 1 ? 2 : 1
 }
 
 template <int BITS, int BM, int S>
+__global__ WQ_GEMM_BOUNDS(S) void gemm_kernel(const float *__restrict__ x, int M, int K, int N,
+                                             const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
+                                             float *__restrict__ y, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[S * 2 * Stage<BITS, BM>::BYTES];
+    // XCD-aware tile order: workgroups id, id+8, id+16, ... run on one XCD; give
+    // them consecutive tiles (row-major over (tm, tn)).
+    const int T = tiles_m * tiles_n;
+    const int per = (T + kXcds - 1) / kXcds;
+    const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (tile >= T) return;
+    const int tm = tile / tiles_n;
+    gemm_tile<BITS, BM, S>(x, M, K, N, q, s, y, tm, tile - tm * tiles_n, lds_all);
+}
+
+// Grouped prefill: the work items of every tensor of a planned table in one
+// launch. Item i belongs to the entry whose [tile_begin, tile_begin + tiles)
+// holds it; within an entry, item j is tile (j % tiles_m, j / tiles_m), so with
+// entries starting at multiples of 8 the items of one XCD (i % 8) share row
+// tiles of x. Items past an entry's tiles (alignment padding) do nothing.
+template <int BM, int S>
+__global__ WQ_GEMM_BOUNDS(S) void gemm_grouped_kernel(const uint8_t *__restrict__ base,
+                                                      const wq_desc *__restrict__ table, int count, int M)
+{
+    // int8 has the largest stage of the three code widths
+    static_assert(Stage<8, BM>::BYTES >= Stage<4, BM>::BYTES && Stage<8, BM>::BYTES >= Stage<5, BM>::BYTES, "");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[S * 2 * Stage<8, BM>::BYTES];
+    const int64_t item = blockIdx.x;
+    const int tiles_m = (M + BM - 1) / BM;
+    int e = -1;
+    for (int i = 0; i < count; ++i) {
+        const int64_t tb = table[i].tile_begin;
+        const int64_t tiles = (int64_t)tiles_m * ((table[i].N + BN - 1) / BN);
+        if (item >= tb && item < tb + tiles) { e = i; break; }
+    }
+    if (e < 0) return;
+    const wq_desc &d = table[e];
+    const int j = (int)(item - d.tile_begin);
+    const int tm = j % tiles_m, tn = j / tiles_m;
+    const int K = (int)d.K, N = (int)d.N;
+    const uint8_t *q = base + d.q_off;
+    const uint16_t *sc = reinterpret_cast<const uint16_t *>(base + d.s_off);
+    if (d.bits == 4) gemm_tile<4, BM, S>(d.x, M, K, N, q, sc, d.y, tm, tn, lds_all);
+    else if (d.bits == 5) gemm_tile<5, BM, S>(d.x, M, K, N, q, sc, d.y, tm, tn, lds_all);
+    else gemm_tile<8, BM, S>(d.x, M, K, N, q, sc, d.y, tm, tn, lds_all);
+}
+
+template <int BITS, int BM, int S>
 hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)
 {
@@ -379,7 +470,27 @@ hipError_t launch_shape(const float *x, int64_t M, int64_t K, int64_t N, const v
     return launch_bits<BITS, 32, 4>(x, M, K, N, q, scales, y, stream);
 }
 
+template <int BM, int S>
+hipError_t launch_grouped(const void *base, const wq_desc *table, int count, int64_t total_tiles, int64_t M,
+                          hipStream_t stream)
+{
+    gemm_grouped_kernel<BM, S><<<(unsigned)total_tiles, kThreads * S, 0, stream>>>(
+        (const uint8_t *)base, table, count, (int)M);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemm_grouped(const void *base, const wq_desc *table, int count, int64_t total_tiles,
+                               int64_t M, hipStream_t stream)
+{
+    static_assert(BN == kGemmTileN, "tile width");
+    const int bm = gemm_grouped_bm(M), sp = gemm_grouped_split(M);
+    if (bm == 32 && sp == 4) return launch_grouped<32, 4>(base, table, count, total_tiles, M, stream);
+    if (bm == 64 && sp == 1) return launch_grouped<64, 1>(base, table, count, total_tiles, M, stream);
+    if (bm == 128 && sp == 1) return launch_grouped<128, 1>(base, table, count, total_tiles, M, stream);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, hipStream_t stream)

@@ -69,13 +69,16 @@ def load(path: Optional[str] = None):
         getattr(lib, f).argtypes = mm
     lib.wq_table_layout.argtypes = [P, I, ctypes.POINTER(ctypes.c_uint64)]
     lib.wq_table_plan.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64)]
+    lib.wq_table_plan_gemm.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64)]
     lib.wq_gemv_grouped.argtypes = [P, P, I, I64, I64, P]
+    lib.wq_gemm_grouped.argtypes = [P, P, I, I64, I64, P]
     lib.wq_embed.argtypes = [P, I64, I64, I64, I, P, P, P, P]
     lib.wq_strerror.argtypes = [I]
     lib.wq_strerror.restype = ctypes.c_char_p
     lib.wq_abi_version.argtypes = []
     for f in ("wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_table_layout",
-              "wq_table_plan", "wq_gemv_grouped", "wq_embed", "wq_abi_version"):
+              "wq_table_plan", "wq_table_plan_gemm", "wq_gemv_grouped", "wq_gemm_grouped", "wq_embed",
+              "wq_abi_version"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -244,6 +247,14 @@ def table_plan(arr, M: int) -> int:
     return int(total.value)
 
 
+def table_plan_gemm(arr, M: int) -> int:
+    """Set tile_begin for a grouped prefill call with M rows; returns the launch size."""
+    total = ctypes.c_int64(0)
+    _check(load().wq_table_plan_gemm(ctypes.addressof(arr) if len(arr) else None, len(arr), M,
+                                     ctypes.byref(total)), "wq_table_plan_gemm")
+    return int(total.value)
+
+
 class Package:
     """One device allocation holding packed tensors at 64-byte-aligned offsets,
     plus its host tensor table."""
@@ -279,9 +290,11 @@ def torch_int16():
 
 
 class GroupedCall:
-    """A planned grouped decode launch: x / y pointers bound into a device table."""
+    """A planned grouped launch: x / y pointers bound into a device table.
+    prefill=False: the decode GEMV of every tensor (wq_gemv_grouped, M <= 16);
+    prefill=True: the prefill GEMM of every tensor (wq_gemm_grouped, any M)."""
 
-    def __init__(self, pkg: Package, xs: Sequence, ys: Sequence, M: int, device="cuda"):
+    def __init__(self, pkg: Package, xs: Sequence, ys: Sequence, M: int, device="cuda", prefill: bool = False):
         torch = _torch()
         _need(len(xs) == len(pkg.specs) and len(ys) == len(pkg.specs), "one x and one y per tensor")
         arr = (WqDesc * len(pkg.specs))()
@@ -292,7 +305,8 @@ class GroupedCall:
             _dev_tensor(y, torch.float32, f"y[{i}]")
             _need(tuple(x.shape) == (M, K) and tuple(y.shape) == (M, N), f"tensor {i}: x/y shape")
             arr[i].x, arr[i].y = _ptr(x), _ptr(y)
-        self.total_tiles = table_plan(arr, M)
+        self.prefill = prefill
+        self.total_tiles = table_plan_gemm(arr, M) if prefill else table_plan(arr, M)
         self.M = M
         self.count = len(pkg.specs)
         self.pkg = pkg
@@ -305,5 +319,6 @@ class GroupedCall:
         self.keep = (list(xs), list(ys))
 
     def __call__(self, stream=None):
-        _check(load().wq_gemv_grouped(self.pkg.base, _ptr(self.table_dev), self.count,
-                                      self.total_tiles, self.M, _stream(stream)), "wq_gemv_grouped")
+        fn = "wq_gemm_grouped" if self.prefill else "wq_gemv_grouped"
+        _check(getattr(load(), fn)(self.pkg.base, _ptr(self.table_dev), self.count,
+                                   self.total_tiles, self.M, _stream(stream)), fn)
