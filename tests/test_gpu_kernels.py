@@ -229,12 +229,14 @@ def test_gemm_parity(torch, bits, K, N):
 
 
 @pytest.mark.parametrize("bits", [4, 5, 8])
-def test_gemm_tall_tiles(torch, bits):
-    """M >= 256 with at least 256 tiles of 128 x 128 takes 128-row tiles; ragged
-    M (2100 = 16 tiles + 52 rows), N (2000 = 15 tiles + 80 columns) and K (three
-    blocks: the last K stage is half past K)."""
-    M, K, N = 2100, 128 if bits == 5 else 96, 2000
-    w = _weights(N, K, (14, bits))
+@pytest.mark.parametrize("N", [2000, 4000])
+def test_gemm_tall_tiles(torch, bits, N):
+    """M >= 256 with at least 256 tiles of 128 x 128 takes 128-row tiles (K loop
+    split in two below 512 tiles: N = 2000; unsplit: N = 4000); ragged M (2100 =
+    16 tiles + 52 rows), N (15 or 31 tiles + 80 columns) and K (three blocks:
+    the last K stage is half past K)."""
+    M, K = 2100, 128 if bits == 5 else 96
+    w = _weights(N, K, (14, bits, N))
     q_ref, s_ref = oracle.quantize(w, bits)
     x = inputs.normal((M, K), seed=(15, bits))
     x[::97] *= 20
