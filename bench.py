@@ -224,6 +224,23 @@ def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
     4096 tokens (the long-prefill length). Each size is captured as a graph of
     `reps` lookups and replayed; the looked-up rows are checked bitwise against
     the oracle on the same rows."""
+    # the same MLP GEMMs (gate, up, down) in one grouped prefill launch
+    mlp = [wl.tensors[i] for i in gemm_idx]
+    pkg = wqa.Package([(t.bits, t.N, t.K) for t in mlp])
+    for j, t in enumerate(mlp):
+        pkg.pack_into(j, torch.from_numpy(wl.weight(t)).cuda())
+    gys = [torch.empty((t.M, t.N), dtype=torch.float32, device="cuda") for t in mlp]
+    gcall = wqa.GroupedCall(pkg, [xs[t.act][t.act_row0: t.act_row0 + t.M] for t in mlp], gys, mlp[0].M,
+                            prefill=True)
+    g_ms, _ = time_grouped(torch, [gcall], max(10, 3 * steps), max(3, warmup))
+    torch.cuda.synchronize()
+    # against the per-call outputs (the down projection's K split differs: fp32
+    # summation order only)
+    g_diff = max(float(torch.linalg.vector_norm(gys[j] - outs[i]) / torch.linalg.vector_norm(outs[i]))
+                 for j, i in enumerate(gemm_idx))
+    if not g_diff <= 1e-5:
+        log(f"grouped MLP outputs differ from wq_linear's: relative {g_diff:.2e}")
+    tflops_grouped = mlp_flops / (g_ms * 1e-3) / 1e12
     lm = [i for i, t in enumerate(wl.tensors) if t.name == "lm_head"][0]
     t = wl.tensors[lm]
     q, sc = pkg.q(lm), pkg.scales(lm)
@@ -358,6 +375,23 @@ def prefill_leg(torch, wqa, inputs, steps, warmup):
     gemm_idx = [i for i, t in enumerate(wl.tensors) if t.name != "lm_head"]
     mlp_flops = sum(2 * wl.tensors[i].M * wl.tensors[i].N * wl.tensors[i].K for i in gemm_idx)
     mlp_ms = sum(per[i] for i in gemm_idx)
+    # the same MLP GEMMs (gate, up, down) in one grouped prefill launch
+    mlp = [wl.tensors[i] for i in gemm_idx]
+    pkg = wqa.Package([(t.bits, t.N, t.K) for t in mlp])
+    for j, t in enumerate(mlp):
+        pkg.pack_into(j, torch.from_numpy(wl.weight(t)).cuda())
+    gys = [torch.empty((t.M, t.N), dtype=torch.float32, device="cuda") for t in mlp]
+    gcall = wqa.GroupedCall(pkg, [xs[t.act][t.act_row0: t.act_row0 + t.M] for t in mlp], gys, mlp[0].M,
+                            prefill=True)
+    g_ms, _ = time_grouped(torch, [gcall], max(10, 3 * steps), max(3, warmup))
+    torch.cuda.synchronize()
+    # against the per-call outputs (the down projection's K split differs: fp32
+    # summation order only)
+    g_diff = max(float(torch.linalg.vector_norm(gys[j] - outs[i]) / torch.linalg.vector_norm(outs[i]))
+                 for j, i in enumerate(gemm_idx))
+    if not g_diff <= 1e-5:
+        log(f"grouped MLP outputs differ from wq_linear's: relative {g_diff:.2e}")
+    tflops_grouped = mlp_flops / (g_ms * 1e-3) / 1e12
     lm = [i for i, t in enumerate(wl.tensors) if t.name == "lm_head"][0]
     lt = wl.tensors[lm]
     lm_bytes = lt.weight_bytes + 4 * lt.M * lt.K + 4 * lt.M * lt.N
@@ -373,6 +407,10 @@ def prefill_leg(torch, wqa, inputs, steps, warmup):
                      "roofline": {"bound": "mfma", "achieved": round(tflops_mlp, 2),
                                   "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(tflops_mlp / MFMA_F16_PEAK_TFLOPS, 4)}},
+        "mlp_gemm_grouped": {"calls": "gate, up, down at M=4096 in one wq_gemm_grouped launch",
+                             "tflops": round(tflops_grouped, 2), "ms": round(g_ms, 4),
+                             "rel_diff_vs_per_call": g_diff,
+                             "frac": round(tflops_grouped / MFMA_F16_PEAK_TFLOPS, 4)},
         "lm_head_m64": {"ms": round(per[lm], 4), "gbs": round(lm_bytes / (per[lm] * 1e-3) / 1e9, 1),
                         "hbm_frac": round(lm_bytes / (per[lm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
