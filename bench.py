@@ -224,23 +224,6 @@ def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
     4096 tokens (the long-prefill length). Each size is captured as a graph of
     `reps` lookups and replayed; the looked-up rows are checked bitwise against
     the oracle on the same rows."""
-    # the same MLP GEMMs (gate, up, down) in one grouped prefill launch
-    mlp = [wl.tensors[i] for i in gemm_idx]
-    pkg = wqa.Package([(t.bits, t.N, t.K) for t in mlp])
-    for j, t in enumerate(mlp):
-        pkg.pack_into(j, torch.from_numpy(wl.weight(t)).cuda())
-    gys = [torch.empty((t.M, t.N), dtype=torch.float32, device="cuda") for t in mlp]
-    gcall = wqa.GroupedCall(pkg, [xs[t.act][t.act_row0: t.act_row0 + t.M] for t in mlp], gys, mlp[0].M,
-                            prefill=True)
-    g_ms, _ = time_grouped(torch, [gcall], max(10, 3 * steps), max(3, warmup))
-    torch.cuda.synchronize()
-    # against the per-call outputs (the down projection's K split differs: fp32
-    # summation order only)
-    g_diff = max(float(torch.linalg.vector_norm(gys[j] - outs[i]) / torch.linalg.vector_norm(outs[i]))
-                 for j, i in enumerate(gemm_idx))
-    if not g_diff <= 1e-5:
-        log(f"grouped MLP outputs differ from wq_linear's: relative {g_diff:.2e}")
-    tflops_grouped = mlp_flops / (g_ms * 1e-3) / 1e12
     lm = [i for i, t in enumerate(wl.tensors) if t.name == "lm_head"][0]
     t = wl.tensors[lm]
     q, sc = pkg.q(lm), pkg.scales(lm)
