@@ -140,8 +140,14 @@ __device__ __forceinline__ void gemm_tile(const float *__restrict__ x, int M, in
         xblk[i] = sl >> 2;
         xlds[i] = aslot(r, sl) * 16;
     }
-    // scales: thread t < BN loads the KT scales of column n0 + t
-    int sn = n0 + (t & (BN - 1));
+    // scales (and int5 bit-4 dwords): a stage needs KT * BN of them, one per
+    // thread: thread t loads block sk = t % KT of the stage for column t / KT,
+    // so the KT lanes of a column read one cache line. Each lane of such a load
+    // reads a different row of the scales; loading each value once, from as few
+    // lines as possible, measured 10-30% faster than KT loads in every thread.
+    static_assert(kThreads == BN * KT, "one scale per thread and stage");
+    const int sk = t % KT;
+    int sn = n0 + t / KT;
     sn = sn < N ? sn : N - 1;
     const uint32_t soff = (uint32_t)sn * (uint32_t)C * 2;
     // codes: thread t loads QI pieces of 16 bytes; piece pc of a stage is piece
@@ -162,8 +168,8 @@ __device__ __forceinline__ void gemm_tile(const float *__restrict__ x, int M, in
     struct Regs {
         f4 xv[XI][2];
         u4 qv[QI];
-        uint16_t sv[KT];
-        uint32_t hv[KT];                          // int5: bit-4 dwords of column sn
+        uint16_t sv;                              // scale of block sk of column sn
+        uint32_t hv;                              // int5: its bit-4 dword
     };
     Regs rs[PF];
     const uint32_t hoff = (uint32_t)sn * qrow + (uint32_t)K / 2;
@@ -189,11 +195,10 @@ __device__ __forceinline__ void gemm_tile(const float *__restrict__ x, int M, in
             xv[i][0] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0));
             xv[i][1] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, o + 16, 0, 0));
         }
-#pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            const int b = b0 + k < C ? b0 + k : C - 1;
-            sv[k] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff + (uint32_t)b * 2, 0, 0);
-            if constexpr (BITS == 5) hv[k] = __builtin_amdgcn_raw_buffer_load_b32(qr, hoff + (uint32_t)b * 4, 0, 0);
+        {
+            const int b = b0 + sk < C ? b0 + sk : C - 1;
+            sv = __builtin_amdgcn_raw_buffer_load_b16(sr, soff + (uint32_t)b * 2, 0, 0);
+            if constexpr (BITS == 5) hv = __builtin_amdgcn_raw_buffer_load_b32(qr, hoff + (uint32_t)b * 4, 0, 0);
         }
     };
     // x rounded to binary16 in operand order, the codes and the scales (zero past
@@ -222,15 +227,13 @@ __device__ __forceinline__ void gemm_tile(const float *__restrict__ x, int M, in
             for (int k = 0; k < 8; ++k) h[operand_slot<BITS>(k)] = (_Float16)v[k];   // nearest even
             *reinterpret_cast<h8 *>(base + xlds[i]) = h;
         }
-        if (t < BN) {
+        {
             uint16_t *Sc = reinterpret_cast<uint16_t *>(base + L::A_BYTES + L::B_BYTES + L::H_BYTES);
-            const int b0 = (st0 + st) * KT;
-#pragma unroll
-            for (int k = 0; k < KT; ++k) Sc[t * KT + k] = b0 + k < C ? sv[k] : (uint16_t)0;
+            const int b = (st0 + st) * KT + sk;
+            Sc[t] = b < C ? sv : (uint16_t)0;    // column t / KT, block sk
             if constexpr (BITS == 5) {
                 uint32_t *H = reinterpret_cast<uint32_t *>(base + L::A_BYTES + L::B_BYTES);
-#pragma unroll
-                for (int k = 0; k < KT; ++k) H[t * KT + k] = hv[k];
+                H[t] = hv;
             }
         }
     };
