@@ -16,10 +16,11 @@
 //    result stays deterministic and no memory beyond y is written.
 //  * The K loop runs over stages of KT = 2 quantization blocks through two LDS
 //    buffers. The packed codes, x (fp32) and the scales of a stage are loaded
-//    into registers while the previous stage is computed, then written to the
-//    other buffer: x rounded to binary16 (nearest even) in the order the unpack
-//    produces the codes, with an XOR swizzle of its 16-byte pieces so that the
-//    128-bit fragment reads of the rows hit distinct banks.
+//    into registers while earlier stages are computed (one stage ahead, two
+//    for 32-row tiles), then written to the free buffer: x rounded to binary16
+//    (nearest even) in the order the unpack produces the codes, with an XOR
+//    swizzle of its 16-byte pieces so that the 128-bit fragment reads of the
+//    rows hit distinct banks. Each scale is loaded by one thread.
 //  * Each block of 32 values is two chained v_mfma_f32_32x32x16_f16 per 32 x 32
 //    fragment from a zero accumulator: the block's fp32 partial, which is then
 //    scaled by the block scale of its column and added to the fp32 accumulator
@@ -33,6 +34,8 @@
 //    modulo 8) cover consecutive tiles of a row of tiles and share x in that
 //    XCD's L2. y is written with non-temporal stores: it is not read again by
 //    this kernel and would otherwise evict x from L2.
+//  * The grouped form runs the tiles of every tensor of a planned table in one
+//    launch (the projections of a layer), with the same tile body.
 #include "wq_internal.h"
 #include "wq_decode.h"
 
