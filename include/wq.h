@@ -26,7 +26,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers on the current HIP device, owned by the
- *     caller; the library allocates nothing and keeps no state.
+ *     caller. The library keeps no state besides one device memory pool per
+ *     device, from which wq_gemm (and wq_linear for M > 16) takes its
+ *     workspace with stream-ordered allocation on the caller's stream (created
+ *     on first use, kept until the process ends); no other entry point
+ *     allocates.
  *   - Arguments are validated on the host before any launch; a non-zero
  *     wq_status is returned and nothing is launched. Requirements: bits in
  *     {4, 5, 8}; K > 0 and K % 32 == 0 (K % 128 == 0 for int5, so rows stay
@@ -108,14 +112,25 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
 /*
  * wq_gemm -- prefill path (the devpost page's blocked prefill GEMM that unpacks
  * each weight group once and reuses it across all activation rows), any M >= 1,
- * tuned for M >= 128. Packed weight tiles are staged in LDS and every code is
- * unpacked exactly once per output tile into binary16 (the integer codes are
- * exact there); x is rounded to binary16 (nearest even); each 32-wide K step is
- * one quantization block, computed by fp16 matrix-core instructions into an
- * fp32 partial that is then scaled by that block's scale.
- * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call.
- * Sizes: M * K * 4 (the bytes of x), N * K * bits / 8 and N * K / 16 must each
- * be below 2^32 (32-bit offsets in the kernel), else WQ_ERR_SHAPE.
+ * tuned for M >= 128. Two kernels on `stream`:
+ *   1. x is rounded to binary16 once per call into a workspace: each row m is
+ *      scaled by a power of two 2^e_m so that its largest magnitude lies in
+ *      [2^14, 2^15), then rounded to nearest even (for rows inside binary16's
+ *      normal range this is exactly the binary16 rounding of x, times 2^e_m);
+ *   2. packed weight tiles are staged in LDS and every code is unpacked exactly
+ *      once per output tile into binary16 (the integer codes are exact there);
+ *      each 32-wide K step is one quantization block, computed by fp16
+ *      matrix-core instructions into an fp32 partial that is scaled by that
+ *      block's scale and accumulated in fp32; y = acc * 2^-e_m.
+ * The workspace (about 2*M*K bytes) comes from the library's stream-ordered
+ * pool on the current device and is released on `stream` after the launch.
+ * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call for finite x whose
+ * rows' largest magnitudes are at least 2^-112 (values below 2^-28 of their
+ * row's largest magnitude are rounded with an absolute error under 2^-39 of
+ * it). A row holding inf or NaN gives non-finite outputs in that row only.
+ * Sizes: M * K * 2, N * K * bits / 8 and N * K / 16 must each be below 2^32
+ * (32-bit offsets in the kernels), else WQ_ERR_SHAPE. A pool allocation
+ * failure is reported as WQ_ERR_HIP.
  */
 int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
             const void *q, const uint16_t *scales, float *y, hipStream_t stream);
@@ -148,7 +163,9 @@ int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits,
  */
 typedef struct wq_desc {
     int32_t bits;          /* 4, 5 or 8 */
-    int32_t reserved;      /* must be 0 */
+    int32_t ws_slot;       /* prefill plans: offset of this entry's prepared x in the
+                              grouped workspace, in 256-byte units (set by
+                              wq_table_plan_gemm); decode plans set it to 0 */
     int64_t N;             /* output features (rows of q) */
     int64_t K;             /* input features, multiple of 32 */
     uint64_t q_off;        /* byte offset of q from the package base, multiple of 64 */
@@ -186,30 +203,37 @@ int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
 
 /*
  * wq_table_plan_gemm -- host only. For a grouped prefill call (wq_gemm_grouped)
- * with M >= 1 rows, set tile_begin of every entry and return the launch size in
- * *total_tiles. Validates every entry as wq_table_plan does, and M * K * 4 <
- * 2^32 for each. Work items are dispatched longest K first (ties in table
- * order), and each entry's items start at a multiple of 8. The tile shape
- * depends on M only, so a plan is valid for exactly the M it was made with.
+ * with M >= 1 rows, set tile_begin and ws_slot of every entry, return the
+ * launch size in *total_tiles and the workspace size in *workspace_bytes.
+ * Validates every entry as wq_table_plan does, and M * K * 2 < 2^32 for each.
+ * Work items are dispatched longest K first (ties in table order), and each
+ * entry's items start at a multiple of 8. Entries that read the same x (same
+ * pointer and K) with the same code order (int8, or int4/int5) share one
+ * workspace slot. The tile shape depends on M only, so a plan is valid for
+ * exactly the M it was made with.
  */
-int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles);
+int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles,
+                       uint64_t *workspace_bytes);
 
 /*
- * wq_gemm_grouped -- one launch that runs the prefill GEMM of every tensor in a
- * planned table (the devpost page's blocked prefill GEMM, "How we built it",
- * over all projections of a layer at once, so that short prefills fill the
- * chip). `table_dev` is a device copy of a table planned by wq_table_plan_gemm
- * with the same M; `base` is the package base (64-byte aligned). Each call's y
- * [M][N] is computed as wq_gemm computes it (same unpack, binary16 rounding of
- * x and per-block fp32 scaling), with one tile shape for the whole launch:
- * 32-row tiles with each tile's K loop split four ways for M <= 128, 64-row tiles
- * for M <= 512, 128-row tiles above. The result is deterministic and meets
- * wq_gemm's error bound; it equals wq_gemm bitwise when both use the same tile
- * shape. The calls must be independent (no call reads another call's y, and
- * the y of different entries do not overlap).
+ * wq_gemm_grouped -- one launch of x preparation and one of the prefill GEMM
+ * over every tensor in a planned table (the devpost page's blocked prefill
+ * GEMM, "How we built it", over all projections of a layer at once, so that
+ * short prefills fill the chip). `table_dev` is a device copy of a table
+ * planned by wq_table_plan_gemm with the same M; `base` is the package base
+ * (64-byte aligned); `workspace` is caller-owned device memory of at least the
+ * planned workspace_bytes, 256-byte aligned (it may be null when that is 0).
+ * Each call's y [M][N] is computed as wq_gemm computes it (same preparation of
+ * x, unpack and per-block fp32 scaling), with one tile shape for the whole
+ * launch: 64-row tiles with each tile's K loop split two ways for M <= 128,
+ * 128-row tiles above. The result is deterministic and meets wq_gemm's error
+ * bound; it equals wq_gemm bitwise when both use the same tile shape. The
+ * calls must be independent (no call reads another call's y, the y of
+ * different entries do not overlap, and no y overlaps the workspace).
  */
 int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count,
-                    int64_t total_tiles, int64_t M, hipStream_t stream);
+                    int64_t total_tiles, int64_t M, void *workspace,
+                    uint64_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text for a wq_status value (static storage). */
 const char *wq_strerror(int status);

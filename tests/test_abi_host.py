@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
             "wq_embed", "wq_abi_version", "wq_table_plan_gemm", "wq_gemm_grouped"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.wq_abi_version() == 4
+    assert lib.wq_abi_version() == 5
 
 
 def test_sizes(lib):
@@ -146,15 +146,20 @@ def test_grouped_validation(lib):
 
 
 def test_gemm_x_offset_limit(lib):
-    """The prefill kernels address x with 32-bit byte offsets: M * K * 4 >= 2^32
-    is refused before anything is launched."""
+    """The prefill kernels address the binary16 copy of x with 32-bit byte
+    offsets: M * K * 2 >= 2^32 is refused before anything is launched."""
     for fn in ("wq_gemm", "wq_linear"):
-        assert getattr(lib, fn)(FAKE, 1 << 20, 1024, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+        assert getattr(lib, fn)(FAKE, 1 << 21, 1024, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
 
 
 def _gemm_items(M, N):
-    bm = 32 if M <= 128 else (64 if M <= 512 else 128)
+    bm = 64 if M <= 128 else 128
     return -(-M // bm) * -(-N // 128)
+
+
+def _ws_bytes(M, K):
+    r = lambda b: -(-b // 256) * 256
+    return r(M * K * 2) + r(M * 4)
 
 
 @pytest.mark.parametrize("M", [1, 100, 128, 129, 512, 513, 1024, 4096])
@@ -167,8 +172,14 @@ def test_table_plan_gemm(lib, M):
     with pytest.raises(wqa.WqError):
         wqa.table_plan_gemm(arr, M)                  # x / y not bound yet
     for i in range(len(specs)):
-        arr[i].x, arr[i].y = FAKE, FAKE
-    total = wqa.table_plan_gemm(arr, M)
+        arr[i].x, arr[i].y = FAKE + 4096 * i, FAKE
+    total, ws = wqa.table_plan_gemm(arr, M)
+    # every entry reads its own x here: one workspace slot each, in table order
+    off = 0
+    for i, (bits, N, K) in enumerate(specs):
+        assert arr[i].ws_slot * 256 == off
+        off += _ws_bytes(M, K)
+    assert ws == off
     order = sorted(range(len(specs)), key=lambda i: (-specs[i][2], i))
     cur = 0
     for i in order:
@@ -188,7 +199,7 @@ def test_table_plan_gemm_validation(lib):
             wqa.table_plan_gemm(arr, M)
         assert e.value.status == MRANGE
     with pytest.raises(wqa.WqError) as e:
-        wqa.table_plan_gemm(arr, 1 << 20)            # M * K * 4 >= 2^32
+        wqa.table_plan_gemm(arr, 1 << 21)            # M * K * 2 >= 2^32
     assert e.value.status == SHAPE
     arr[1].y = MIS
     with pytest.raises(wqa.WqError) as e:
@@ -200,25 +211,42 @@ def test_table_plan_gemm_validation(lib):
         wqa.table_plan_gemm(arr, 64)
     assert e.value.status == BITS
     arr[0].bits = 4
-    arr[0].reserved = 1
-    with pytest.raises(wqa.WqError) as e:
-        wqa.table_plan_gemm(arr, 64)
-    assert e.value.status == TABLE
-    arr[0].reserved = 0
-    assert wqa.table_plan_gemm(arr, 64) > 0
+    total, ws = wqa.table_plan_gemm(arr, 64)
+    assert total > 0 and ws == _ws_bytes(64, 1024) + _ws_bytes(64, 64)
     empty = (W.WqDesc * 0)()
-    assert wqa.table_plan_gemm(empty, 64) == 0
+    assert wqa.table_plan_gemm(empty, 64) == (0, 0)
+
+
+def test_table_plan_gemm_shared_inputs(lib):
+    """Entries reading the same x (pointer and K) with the same code order share
+    a workspace slot; int8 (its own operand order) gets a slot of its own."""
+    specs = [(4, 2048, 1024), (4, 1024, 1024), (8, 1024, 1024), (5, 512, 1024), (4, 1024, 3072),
+             (8, 256, 1024)]
+    arr, _ = wqa.table_layout(specs)
+    xa, xb = FAKE, FAKE + 4096
+    for i, x in enumerate([xa, xa, xa, xa, xb, xa]):
+        arr[i].x, arr[i].y = x, FAKE
+    M = 200
+    _, ws = wqa.table_plan_gemm(arr, M)
+    s = [arr[i].ws_slot for i in range(len(specs))]
+    assert s[0] == s[1] == s[3] == 0                  # int4 / int5 order, x_a
+    assert s[2] == s[5] == _ws_bytes(M, 1024) // 256  # int8 order, x_a
+    assert s[4] == 2 * _ws_bytes(M, 1024) // 256      # x_b (K = 3072)
+    assert ws == 2 * _ws_bytes(M, 1024) + _ws_bytes(M, 3072)
 
 
 def test_gemm_grouped_validation(lib):
-    assert lib.wq_gemm_grouped(FAKE, FAKE, 3, 10, 0, None) == MRANGE
-    assert lib.wq_gemm_grouped(FAKE, FAKE, 3, 10, (1 << 30) + 1, None) == MRANGE
-    assert lib.wq_gemm_grouped(FAKE, FAKE, -1, 10, 64, None) == SHAPE
-    assert lib.wq_gemm_grouped(FAKE, FAKE, 3, 1 << 31, 64, None) == SHAPE
-    assert lib.wq_gemm_grouped(None, FAKE, 3, 10, 64, None) == NULL
-    assert lib.wq_gemm_grouped(FAKE + 16, FAKE, 3, 10, 64, None) == ALIGN
-    assert lib.wq_gemm_grouped(FAKE, FAKE + 16, 3, 10, 64, None) == ALIGN
-    assert lib.wq_gemm_grouped(None, None, 0, 0, 64, None) == OK
+    g = lib.wq_gemm_grouped
+    assert g(FAKE, FAKE, 3, 10, 0, FAKE, 256, None) == MRANGE
+    assert g(FAKE, FAKE, 3, 10, (1 << 30) + 1, FAKE, 256, None) == MRANGE
+    assert g(FAKE, FAKE, -1, 10, 64, FAKE, 256, None) == SHAPE
+    assert g(FAKE, FAKE, 3, 1 << 31, 64, FAKE, 256, None) == SHAPE
+    assert g(None, FAKE, 3, 10, 64, FAKE, 256, None) == NULL
+    assert g(FAKE, FAKE, 3, 10, 64, None, 256, None) == NULL
+    assert g(FAKE + 16, FAKE, 3, 10, 64, FAKE, 256, None) == ALIGN
+    assert g(FAKE, FAKE + 16, 3, 10, 64, FAKE, 256, None) == ALIGN
+    assert g(FAKE, FAKE, 3, 10, 64, FAKE + 64, 256, None) == ALIGN
+    assert g(None, None, 0, 0, 64, None, 0, None) == OK
 
 
 def test_strerror(lib):

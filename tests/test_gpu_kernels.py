@@ -231,7 +231,7 @@ def test_gemm_parity(torch, bits, K, N):
 @pytest.mark.parametrize("bits", [4, 5, 8])
 @pytest.mark.parametrize("N", [2000, 4000])
 def test_gemm_tall_tiles(torch, bits, N):
-    """M >= 256 with at least 256 tiles of 128 x 128 takes 128-row tiles (K loop
+    """M > 64 with at least 256 tiles of 128 x 128 takes 128-row tiles (K loop
     split in two below 512 tiles: N = 2000; unsplit: N = 4000); ragged M (2100 =
     16 tiles + 52 rows), N (15 or 31 tiles + 80 columns) and K (three blocks:
     the last K stage is half past K)."""
@@ -365,9 +365,9 @@ GROUPED_GEMM_SPECS = [(4, 2048, 1024), (8, 300, 1024), (4, 1024, 2048), (5, 130,
 @pytest.mark.parametrize("M", [1, 17, 100, 128, 130, 512, 600])
 def test_gemm_grouped_matches_oracle(torch, M):
     """One grouped prefill launch over int4 / int5 / int8 tensors with ragged N
-    and short and long K, at M covering the three tile shapes (32 rows split four
-    ways, 64 rows, 128 rows) and their ragged tails; every output is written
-    (y starts as NaN) and meets the GEMM bound against the oracle."""
+    and short and long K, at M covering both tile shapes (64 rows with the K
+    loop split two ways, 128 rows) and their ragged tails; every output is
+    written (y starts as NaN) and meets the GEMM bound against the oracle."""
     specs = GROUPED_GEMM_SPECS
     pkg = wqa.Package(specs)
     refs = []
@@ -400,9 +400,9 @@ def test_gemm_grouped_matches_oracle(torch, M):
 
 
 def test_gemm_grouped_bitwise_as_single(torch):
-    """With the same tile shape (M <= 128, K >= 224 and few tiles: 32-row tiles,
-    K split four ways, in both paths) the grouped launch equals wq_gemm bitwise;
-    the same table run twice gives the same bits."""
+    """With the same tile shape (M <= 128 and few tiles: 64-row tiles, K split
+    two ways, in both paths) the grouped launch equals wq_gemm bitwise; the same
+    table run twice gives the same bits."""
     M = 100
     specs = [(4, 1000, 256), (8, 256, 512), (5, 300, 256), (4, 129, 1024)]
     pkg = wqa.Package(specs)

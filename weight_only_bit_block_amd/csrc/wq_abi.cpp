@@ -3,13 +3,56 @@
 //
 // Every check runs on the host before anything is launched; a failing check
 // returns a status and touches no HIP state. Launches go to the caller's
-// stream; nothing is allocated, synchronized or cached here.
+// stream; nothing is synchronized here. The only allocation is the prefill
+// workspace of wq_gemm, taken from a per-device stream-ordered memory pool.
 #include <stdint.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "wq_internal.h"
 
 namespace {
+
+// ---------------------------------------------------------------- workspace pool
+// One pool per device, created on first use and kept until the process ends
+// (its release threshold is the maximum, so freed blocks stay in the pool and
+// later calls on any stream reuse them without returning to the driver).
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
+hipError_t pool_alloc(void **p, size_t bytes, hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    hipMemPool_t pool;
+    {
+        std::lock_guard<std::mutex> lk(g_pool_mu);
+        if (!g_pools[dev]) {
+            hipMemPoolProps props;
+            memset(&props, 0, sizeof props);
+            props.allocType = hipMemAllocationTypePinned;
+            props.handleTypes = hipMemHandleTypeNone;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            hipMemPool_t created = nullptr;
+            e = hipMemPoolCreate(&created, &props);
+            if (e != hipSuccess) return e;
+            uint64_t keep = UINT64_MAX;
+            e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
+            if (e != hipSuccess) {
+                (void)hipMemPoolDestroy(created);
+                return e;
+            }
+            g_pools[dev] = created;
+        }
+        pool = g_pools[dev];
+    }
+    return hipMallocFromPoolAsync(p, bytes, pool, stream);
+}
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;     // bound on M, N, K (index arithmetic)
 constexpr int64_t kMaxK = (int64_t)1 << 24;
@@ -59,14 +102,22 @@ inline int gemv_offsets_ok(int64_t K, int64_t N, int bits)
     return WQ_OK;
 }
 
-// The prefill kernels address x (fp32, M x K) with 32-bit byte offsets.
-inline bool gemm_x_ok(int64_t M, int64_t K) { return (uint64_t)M * (uint64_t)K * 4 < ((uint64_t)1 << 32); }
-
 int gemm_grid_ok(int64_t M, int64_t N)
 {
     // the prefill tile is 64 x 128; the grid is rounded up to a multiple of 8
     const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
     return tiles <= (int64_t)0x7FFFFFF0 ? WQ_OK : WQ_ERR_SHAPE;
+}
+
+// Limits of the prefill kernels: 32-bit byte offsets into the prepared x
+// (binary16, M x K), the codes and the scales.
+int gemm_sizes_ok(int64_t M, int64_t K, int64_t N, int bits)
+{
+    const uint64_t lim = (uint64_t)1 << 32;
+    if ((uint64_t)M * (uint64_t)K * 2 >= lim) return WQ_ERR_SHAPE;
+    if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= lim) return WQ_ERR_SHAPE;
+    if ((uint64_t)N * (uint64_t)(K / WQ_BLOCK) * 2 >= lim) return WQ_ERR_SHAPE;
+    return gemm_grid_ok(M, N);
 }
 
 // Checks of one tensor-table entry of a grouped call with M rows.
@@ -80,7 +131,6 @@ int check_entry(const wq_desc &d, int64_t M)
     if (st) return st;
     st = gemv_offsets_ok(d.K, d.N, d.bits);
     if (st) return st;
-    if (d.reserved != 0) return WQ_ERR_TABLE;
     if ((d.q_off % WQ_TABLE_ALIGN) || (d.s_off % WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
     if (d.s_off < d.q_off + (uint64_t)d.N * (uint64_t)d.K * (uint64_t)d.bits / 8 &&
         d.q_off < d.s_off + (uint64_t)d.N * (uint64_t)(d.K / WQ_BLOCK) * 2 && d.N > 0)
@@ -158,13 +208,13 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     int st = check_matmul(x, M, K, N, bits, q, scales, y, &empty);
     if (st) return st;
     if (empty) return WQ_OK;
-    st = gemm_grid_ok(M, N);
+    st = gemm_sizes_ok(M, K, N, bits);
     if (st) return st;
-    // the prefill kernel addresses codes, scales and x (fp32) with 32-bit byte offsets
-    if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= ((uint64_t)1 << 32) || !gemm_x_ok(M, K) ||
-        (uint64_t)N * (uint64_t)(K / WQ_BLOCK) * 2 >= ((uint64_t)1 << 32))
-        return WQ_ERR_SHAPE;
-    return hip_status(wq::launch_gemm(x, M, K, N, bits, q, scales, y, stream));
+    void *ws = nullptr;
+    if (pool_alloc(&ws, (size_t)wq::gemm_ws_bytes(M, K), stream) != hipSuccess) return WQ_ERR_HIP;
+    const hipError_t e = wq::launch_gemm(x, M, K, N, bits, q, scales, y, ws, stream);
+    const hipError_t f = hipFreeAsync(ws, stream);
+    return (e == hipSuccess && f == hipSuccess) ? WQ_OK : WQ_ERR_HIP;
 }
 
 int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits, const void *q,
@@ -227,6 +277,7 @@ int wq_table_plan(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
         const int st = check_entry(d, M);
         if (st) return st;
         d.tile_begin = cur;
+        d.ws_slot = 0;
         const int64_t rows = wq::decode_item_rows(d.K, d.bits, d.N, true, M);
         cur += (d.N + rows - 1) / rows;
         if (cur > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
@@ -247,15 +298,35 @@ int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count, int64
     return hip_status(wq::launch_gemv_grouped(base, table_dev, count, total_tiles, M, stream));
 }
 
-int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles)
+int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles, uint64_t *workspace_bytes)
 {
     if (count < 0) return WQ_ERR_SHAPE;
-    if (!total_tiles || (count > 0 && !table)) return WQ_ERR_NULL;
+    if (!total_tiles || !workspace_bytes || (count > 0 && !table)) return WQ_ERR_NULL;
     if (M < 1 || M > kMaxDim) return WQ_ERR_M_RANGE;
     for (int i = 0; i < count; ++i) {
         const int st = check_entry(table[i], M);
         if (st) return st;
-        if (!gemm_x_ok(M, table[i].K)) return WQ_ERR_SHAPE;
+        const int sz = gemm_sizes_ok(M, table[i].K, table[i].N, table[i].bits);
+        if (sz) return sz;
+    }
+    // workspace slots: one per distinct (x, K, code order) of the non-empty
+    // entries, in table order
+    uint64_t ws = 0;
+    for (int i = 0; i < count; ++i) {
+        wq_desc &d = table[i];
+        d.ws_slot = 0;
+        if (d.N == 0) continue;
+        const bool ord8 = d.bits == 8;
+        int owner = -1;
+        for (int j = 0; j < i && owner < 0; ++j)
+            if (table[j].N > 0 && table[j].x == d.x && table[j].K == d.K && (table[j].bits == 8) == ord8) owner = j;
+        if (owner >= 0) {
+            d.ws_slot = table[owner].ws_slot;
+            continue;
+        }
+        if (ws / wq::kGemmWsUnit > (uint64_t)INT32_MAX) return WQ_ERR_SHAPE;
+        d.ws_slot = (int32_t)(ws / wq::kGemmWsUnit);
+        ws += wq::gemm_ws_bytes(M, d.K);
     }
     // dispatch order: longest K first (the longest K loops start first), ties in
     // table order; each entry starts at a multiple of 8 work items
@@ -276,18 +347,23 @@ int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tile
         prev = k;
     }
     *total_tiles = cur;
+    *workspace_bytes = ws;
     return WQ_OK;
 }
 
-int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_tiles,
-                    int64_t M, hipStream_t stream)
+int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_tiles, int64_t M,
+                    void *workspace, uint64_t workspace_bytes, hipStream_t stream)
 {
     if (M < 1 || M > kMaxDim) return WQ_ERR_M_RANGE;
     if (count < 0 || total_tiles < 0 || total_tiles > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
+    if (count > 65535) return WQ_ERR_SHAPE;                 // one preparation grid row per entry
     if (count == 0 || total_tiles == 0) return WQ_OK;
     if (!base || !table_dev) return WQ_ERR_NULL;
-    if (!aligned(base, WQ_TABLE_ALIGN) || !aligned(table_dev, WQ_TABLE_ALIGN)) return WQ_ERR_ALIGN;
-    return hip_status(wq::launch_gemm_grouped(base, table_dev, count, total_tiles, M, stream));
+    if (workspace_bytes > 0 && !workspace) return WQ_ERR_NULL;
+    if (!aligned(base, WQ_TABLE_ALIGN) || !aligned(table_dev, WQ_TABLE_ALIGN) ||
+        !aligned(workspace, (uintptr_t)wq::kGemmWsUnit))
+        return WQ_ERR_ALIGN;
+    return hip_status(wq::launch_gemm_grouped(base, table_dev, count, total_tiles, M, workspace, stream));
 }
 
 const char *wq_strerror(int status)
@@ -305,6 +381,6 @@ const char *wq_strerror(int status)
     }
 }
 
-int wq_abi_version(void) { return 4; }
+int wq_abi_version(void) { return 5; }
 
 }  // extern "C"

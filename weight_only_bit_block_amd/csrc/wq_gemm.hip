@@ -1,41 +1,57 @@
-// wq_gemm.hip -- prefill GEMM for block-32 int4 / int5 / int8 weights (any M, tuned for M >= 128).
+// wq_gemm.hip -- prefill GEMM for block-32 int4 / int5 / int8 weights (any M >= 1).
 //
 // The TinyMOSS-Diarize devpost page ("How we built it") describes a blocked
 // prefill GEMM that unpacks each weight group once and reuses it across all
-// activation rows. On gfx950 (wave64, fp16 matrix cores, 160 KiB LDS):
+// activation rows, with FP32 activations and dequantization fused into the
+// matmul. On gfx950 (wave64, fp16 matrix cores, 160 KiB LDS per compute unit)
+// the work is done in two kernels on the caller's stream:
 //
-//  * A group of 4 wavefronts computes a BM x 128 tile of y (BM = 128 for long
-//    prefills, 64, or 32 for small problems); wavefront w owns 32 output
-//    columns and all BM rows (BM/32 fragments of 32 x 32), so each weight code
-//    of the tile is unpacked exactly once, in the registers of the wavefront
-//    that uses it, into an exact binary16 integer, and that unpack feeds every
-//    row fragment.
-//  * When there are too few tiles to occupy the chip, a workgroup holds S = 2
-//    or 4 such groups that split the tile's K loop; groups 1..S-1 hand their
-//    fp32 sums to group 0 through LDS, which adds them in group order, so the
-//    result stays deterministic and no memory beyond y is written.
-//  * The K loop runs over stages of KT = 2 quantization blocks through two LDS
-//    buffers. The packed codes, x (fp32) and the scales of a stage are loaded
-//    into registers while earlier stages are computed (one stage ahead, two
-//    for 32-row tiles), then written to the free buffer: x rounded to binary16
-//    (nearest even) in the order the unpack produces the codes, with an XOR
-//    swizzle of its 16-byte pieces so that the 128-bit fragment reads of the
-//    rows hit distinct banks. Each scale is loaded by one thread.
-//  * Each block of 32 values is two chained v_mfma_f32_32x32x16_f16 per 32 x 32
-//    fragment from a zero accumulator: the block's fp32 partial, which is then
-//    scaled by the block scale of its column and added to the fp32 accumulator
-//    (one fused multiply-add per output and block), while the matrix work of
-//    the compute unit's other wavefronts runs. The 32x32x16 shape is used
-//    rather than 16x16x32 because on gfx950 it sustains twice the fp16 matrix
-//    throughput per instruction issued.
-//  * Within a block the 32 values are visited in the order the unpack produces
-//    them, identically for x and the weights, so each dot product is unchanged.
-//  * Tiles are ordered so that the workgroups placed on one XCD (workgroup id
-//    modulo 8) cover consecutive tiles of a row of tiles and share x in that
-//    XCD's L2. y is written with non-temporal stores: it is not read again by
-//    this kernel and would otherwise evict x from L2.
-//  * The grouped form runs the tiles of every tensor of a planned table in one
-//    launch (the projections of a layer), with the same tile body.
+//  1. xprep_kernel rounds x to binary16 once per call, into a workspace: each
+//     row m is first scaled by a power of two 2^e_m chosen so that its largest
+//     magnitude lands in [2^14, 2^15) (for x inside binary16's normal range
+//     this changes nothing but the exponent: the rounded values are the plain
+//     binary16 rounding of x times 2^e_m, and any finite row is representable),
+//     and 2^-e_m is kept per row. Within each block of 32 values the prepared
+//     row is stored in the order in which the matrix instructions consume it
+//     (below), so that the GEMM copies it to LDS without touching it.
+//  2. gemm_kernel: a workgroup of WN x SK wavefronts computes a BM x (32 WN)
+//     tile of y. Wavefront (h, w) owns 32 output columns and all BM rows (BM/32
+//     row fragments of 32 x 32) for the h-th of SK slices of the K loop, so
+//     each weight code is unpacked exactly once per tile, in the registers of
+//     the wavefront that uses it, into an exact binary16 integer, and that
+//     unpack feeds every row fragment.
+//
+// Data movement: the K loop runs over stages of two quantization blocks. The
+// prepared x of a stage (BM rows x 128 bytes), the packed codes and the block
+// scales of the wavefront's 32 columns are copied from global memory straight
+// into LDS by buffer loads with the LDS-direct form (no registers, no vector
+// ALU work), into a ring of NS stage buffers: while stage s is computed the
+// copies of stages s+1 .. s+NS-1 are in flight. Each stage starts with a wait
+// for this wavefront's copies of the stage and one workgroup barrier.
+//
+// Matrix work: per block of 32 values and 32 x 32 fragment, two chained
+// v_mfma_f32_32x32x16_f16 from a zero accumulator give the block's fp32
+// partial, which is scaled by the block scale of its column and added to the
+// fp32 accumulator (one fused multiply-add per output and block). Lane (c, g)
+// of a wavefront (c = lane % 32, g = lane / 32) supplies, for K-step st of a
+// block, the 8 codes of group q = 2g + st of its column (codes 8q .. 8q+7),
+// and the x operand lane (row, g) supplies the same 8 k in the same order
+// (the order the unpack produces them), so each dot product is unchanged.
+// Lane (c, g) therefore reads the contiguous bytes of groups 2g and 2g+1 of a
+// block. The prepared x stores the four groups of a block at positions
+// 2 st + g, i.e. in group order 0, 2, 1, 3.
+//
+// LDS layout: a row of the stage's x occupies 128 bytes (8 slots of 16 bytes,
+// slot 4 kb + 2 st + g); slot s of row r is stored at slot s ^ ((r >> 1) & 7),
+// so the 16 lanes of each 128-bit operand read hit distinct banks. The copy
+// instruction writes 64 consecutive 16-byte slots, so the swizzle is applied
+// by choosing which global piece each lane fetches.
+//
+// Tiles are ordered so that the workgroups placed on one XCD (workgroup id
+// modulo 8) cover consecutive tiles of a row of tiles and share x in that
+// XCD's L2; y is written with non-temporal stores, scaled by the row's 2^-e_m.
+// The grouped form runs the tiles of every tensor of a planned table in one
+// launch (the projections of a layer), with the same tile body.
 #include "wq_internal.h"
 #include "wq_decode.h"
 
@@ -46,363 +62,410 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BN = 128;            // columns per workgroup tile (32 per wavefront)
-constexpr int KT = 2;              // quantization blocks per stage
-constexpr int kThreads = 256;
+constexpr int KT = 2;          // quantization blocks per stage
 constexpr int kXcds = 8;
 
-// LDS layout of one stage buffer (BM rows per workgroup tile: 32, 64 or 128).
-//   A: x as binary16, [BM rows][KT*32 values]; row pitch 128 bytes, 16-byte
-//      slot s of row r stored at slot s ^ ((r >> 1) & 7).
-//   B: packed codes, [BN columns][KT * CB bytes] (int5: the low nibbles), each
-//      column in 8-byte units rotated as CodeUnits describes.
-//   H: int5 only, bit 4 of the codes, [BN columns][KT dwords].
-//   S: binary16 scales, [BN columns][KT].
-template <int BITS, int BM>
-struct Stage {
-    static constexpr int CB = BITS == 8 ? 32 : 16;         // code bytes per column per block (int5: nibbles)
-    static constexpr int A_BYTES = BM * KT * 64;
-    static constexpr int B_BYTES = BN * KT * CB;
-    static constexpr int H_BYTES = BITS == 5 ? BN * KT * 4 : 0;   // int5: bit 4 of the codes
-    static constexpr int S_BYTES = BN * KT * 2;
-    static constexpr int BYTES = A_BYTES + B_BYTES + H_BYTES + S_BYTES;
-};
+// ---------------------------------------------------------------- prepared x
 
-__device__ __forceinline__ int aslot(int r, int s) { return r * (KT * 4) + (s ^ ((r >> 1) & 7)); }
+// Position, within a block, of natural group q (codes 8q .. 8q+7): group q is
+// used by K-step st = q & 1 in lane half g = q >> 1, and stored at 2 st + g.
+__device__ __forceinline__ constexpr int group_pos(int q) { return ((q & 1) << 1) | (q >> 1); }
 
-// B holds column c's KT * CB code bytes in 8-byte units rotated by a
-// column-dependent amount, so that the code reads of a wavefront's 32 columns
-// (one unit index for all of them) hit distinct banks: unit u of column c is
-// stored at unit (u + rot(c)) % P.
-template <int CB>
-struct CodeUnits {
-    static constexpr int COLB = KT * CB;                 // bytes per column
-    static constexpr int P = COLB / 8;                   // units per column (4 or 8)
-    static constexpr int L = COLB == 32 ? 3 : 2;         // columns c, c + 2^L, ... share banks
-    __device__ static constexpr int rot(int c) { return (c >> L) & (P - 1); }
-    __device__ static constexpr int off(int c, int u) { return c * COLB + ((u + rot(c)) & (P - 1)) * 8; }
-};
-
-// Launch bounds of a workgroup of S groups: one 256-thread group (two
-// workgroups per compute unit) or S groups of 256 threads.
-#define WQ_GEMM_BOUNDS(S) __launch_bounds__(((S) == 1 ? kThreads : kThreads * (S)), ((S) == 1 ? 2 : 1))
-
-// Stages whose loads are in flight while one is computed: 2 for 32-row tiles
-// (short prefills, where a stage's few matrix instructions cannot cover a
-// memory round trip), else 1 (registers are needed for the row fragments).
-constexpr int gemm_prefetch(int BM) { return BM == 32 ? 2 : 1; }
-
-// One BM x 128 output tile (tm, tn) of y = x W^T; every thread of the
-// workgroup calls it. lds_all holds at least S * 2 * Stage<BITS, BM>::BYTES.
-template <int BITS, int BM, int S, int PF = gemm_prefetch(BM)>
-__device__ __forceinline__ void gemm_tile(const float *__restrict__ x, int M, int K, int N,
-                                          const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
-                                          float *__restrict__ y, int tm, int tn, uint8_t *lds_all)
+// Power-of-two exponent e for a row whose largest magnitude is amax: amax * 2^e
+// lands in [2^14, 2^15). Rows of zeros or with non-finite entries get e = 0;
+// e is capped so that 2^-e stays a normal fp32 number.
+__device__ __forceinline__ int row_exponent(float amax)
 {
-    using L = Stage<BITS, BM>;
-    constexpr int CB = L::CB;
-    constexpr int RF = BM / 32;                     // 32-row fragments per wavefront
-    constexpr int XI = BM * KT * 4 / kThreads;      // 8-value x groups per thread per stage (4 or 2)
-    constexpr int BP = BN * KT * CB / 16;           // 16-byte code pieces per stage (256 or 512)
-    constexpr int QI = BP / kThreads;               // code pieces per thread per stage (1 or 2)
-    static_assert(XI * kThreads == BM * KT * 4 && BP % kThreads == 0, "tile shape");
-    // S groups of 4 wavefronts split the K loop; each group has its own two stage
-    // buffers, and the partial sums of groups 1..S-1 are reduced through them.
-    static_assert((S - 1) * kThreads * RF * 16 * 4 <= S * 2 * L::BYTES, "reduction fits the stage buffers");
-    const int m0 = tm * BM, n0 = tn * BN;
+    if (!(amax > 0.0f) || !(amax <= 3.4028234663852886e38f)) return 0;
+    int E;
+    (void)frexpf(amax, &E);                  // amax = f * 2^E, f in [0.5, 1)
+    int e = 15 - E;
+    return e > 126 ? 126 : e;                // E >= -125 here except for fp32 subnormals
+}
 
-    const int t = threadIdx.x & (kThreads - 1);  // index within the K group
-    const int h = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kThreads);   // K group
-    const int lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+// One row of x -> binary16 in the prepared layout; one wavefront per row.
+template <int ORDER>
+__device__ __forceinline__ void xprep_row(const float *__restrict__ xrow, int K, _Float16 *__restrict__ orow,
+                                          float *__restrict__ rinv_m, int lane)
+{
+    const int G = K >> 3;                    // groups of 8 values
+    float amax = 0.0f;
+    for (int q = lane; q < G; q += 64) {
+        const f4 a = *reinterpret_cast<const f4 *>(xrow + 8 * q);
+        const f4 b = *reinterpret_cast<const f4 *>(xrow + 8 * q + 4);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const int e = row_exponent(amax);
+    for (int q = lane; q < G; q += 64) {
+        const f4 a = *reinterpret_cast<const f4 *>(xrow + 8 * q);
+        const f4 b = *reinterpret_cast<const f4 *>(xrow + 8 * q + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        h8 h;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            h[operand_slot<ORDER == 1 ? 8 : 4>(k)] = (_Float16)ldexpf(v[k], e);   // exact scaling, then nearest even
+        const int blk = q >> 2;
+        *reinterpret_cast<h8 *>(orow + blk * 32 + group_pos(q & 3) * 8) = h;
+    }
+    if (lane == 0) *rinv_m = ldexpf(1.0f, -e);
+}
+
+// Prepared rows of one x [M][K]: four rows per workgroup.
+template <int ORDER>
+__global__ __launch_bounds__(256) void xprep_kernel(const float *__restrict__ x, int M, int K,
+                                                     _Float16 *__restrict__ x16, float *__restrict__ rinv)
+{
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    xprep_row<ORDER>(x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
+}
+
+// Grouped: entry e (blockIdx.y) prepares its x unless it is empty or an earlier
+// non-empty entry owns the same workspace slot (entries that share an x and a
+// code order share a slot).
+__global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__restrict__ table, int count, int M,
+                                                             uint8_t *__restrict__ ws)
+{
+    const int e = blockIdx.y;
+    const wq_desc &d = table[e];
+    if (d.N == 0) return;                       // no work, and x may be unset
+    const int slot = d.ws_slot;
+    for (int i = 0; i < e; ++i)
+        if (table[i].N > 0 && table[i].ws_slot == slot) return;   // prepared by entry i
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const int K = (int)d.K;
+    uint8_t *base = ws + (size_t)slot * kGemmWsUnit;
+    _Float16 *x16 = reinterpret_cast<_Float16 *>(base);
+    float *rinv = reinterpret_cast<float *>(base + gemm_ws_x16_bytes(M, K));
+    if (d.bits == 8) xprep_row<1>(d.x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
+    else xprep_row<0>(d.x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
+}
+
+// ---------------------------------------------------------------- GEMM tile
+
+// LDS of one stage of one K slice: the prepared x (BM rows x 128 bytes), then for
+// each of the WN wavefronts its codes (B), int5 bit-4 dwords (H) and scales (S:
+// for each (block, column) the aligned dword holding that block's scale).
+template <int BITS, int BM, int WN>
+struct Lay {
+    static constexpr int A = BM * 128;
+    static constexpr int BW = 32 * KT * (BITS == 8 ? 32 : 16);   // codes of 32 columns
+    static constexpr int HW = BITS == 5 ? 32 * KT * 4 : 0;
+    static constexpr int SW = 32 * KT * 4;
+    static constexpr int WAVE = BW + HW + SW;
+    static constexpr int STAGE = A + WN * WAVE;
+};
+template <int BM, int WN>
+constexpr int stage_max() { return Lay<8, BM, WN>::STAGE; }   // int8 has the largest stage
+static_assert(Lay<8, 128, 4>::STAGE >= Lay<5, 128, 4>::STAGE && Lay<8, 32, 4>::STAGE >= Lay<5, 32, 4>::STAGE, "");
+
+// Buffer loads in the LDS-direct form: lane i writes its 16 (4) bytes at LDS
+// byte address lds + 16 i (4 i); lds (in M0) and the resource are uniform. They
+// are issued from inline assembly so that the compiler keeps no wait counting
+// of its own for them (its alias tracking of such copies cannot tell the ring
+// buffers apart and would drain the ring at every stage); every wait on them is
+// the explicit vmcnt wait of the K loop. They write no registers.
+typedef uint32_t sgpr4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ sgpr4 raw_rsrc(const void *p, uint64_t bytes)
+{
+    const uint64_t a = (uint64_t)p;
+    sgpr4 r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);   // stride 0
+    r.z = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    r.w = 0x00020000u;                                                    // 32-bit untyped data
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+__device__ __forceinline__ void dma16(sgpr4 r, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    // s_nop: one wait state between the write of M0 and its read by the copy
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(sgpr4 r, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Launch bounds: workgroups of WN * SK wavefronts; 2 resident per compute unit
+// for 4-wavefront groups.
+#define WQ_GEMM_BOUNDS(WN, SK) __launch_bounds__((WN) * (SK) * 64, ((WN) * (SK) <= 4 ? 2 : 1))
+
+template <int BITS, int BM, int WN, int SK, int NS>
+struct Tile {
+    using L = Lay<BITS, BM, WN>;
+    static constexpr int RF = BM / 32;                  // row fragments per wavefront
+    static constexpr int AI = BM / (8 * WN);            // x copy instructions per wavefront and stage
+    static constexpr int BI = BITS == 8 ? 2 : 1;        // code copy instructions
+    static constexpr int V = AI + BI + (BITS == 5 ? 1 : 0) + 1;   // copies per wavefront and stage
+    static constexpr int SLICE = stage_max<BM, WN>();   // bytes of one K slice in a ring buffer
+    static_assert(AI * 8 * WN == BM, "x rows per copy instruction");
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    static_assert(V * (NS - 2) < 64, "vmcnt");
+};
+
+// One BM x (32 WN) output tile (tm, tn) of y = x W^T; every thread of the
+// workgroup calls it. ring0..ring3 are the NS stage buffers (separate LDS
+// objects, so waits on copies into one never hold reads of another), each of
+// SK * SLICE bytes. x16 / rinv: the prepared x of this call.
+template <int BITS, int BM, int WN, int SK, int NS>
+__device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, const float *__restrict__ rinv,
+                                          int M, int K, int N, const uint8_t *__restrict__ q,
+                                          const uint16_t *__restrict__ s, float *__restrict__ y, int tm, int tn,
+                                          uint8_t *ring0, uint8_t *ring1, uint8_t *ring2, uint8_t *ring3)
+{
+    using T = Tile<BITS, BM, WN, SK, NS>;
+    using L = typename T::L;
+    constexpr int RF = T::RF, AI = T::AI, V = T::V, SLICE = T::SLICE;
+    constexpr int BN = 32 * WN;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int h = wv / WN;                       // K slice
+    const int w = wv - h * WN;                   // wavefront within the slice: columns 32w .. 32w+31
     const int C = K >> 5;                        // blocks per row
     const int NT = (C + KT - 1) / KT;            // stages of the whole K loop
-    const int NTh = (NT + S - 1) / S;            // stages of this group (past K: scale 0)
-    const int st0 = h * NTh;                     // its first stage
-    uint8_t *const lds = lds_all + h * 2 * L::BYTES;
+    const int NTh = (NT + SK - 1) / SK;          // stages of each slice (past K: scale 0)
+    const int st0 = h * NTh;
+    const uint32_t qrow = (uint32_t)K * BITS / 8;
+
+    const sgpr4 xr = raw_rsrc(x16, (uint64_t)M * K * 2);
+    const sgpr4 qr = raw_rsrc(q, (uint64_t)N * qrow);
+    // Scales are copied as the aligned dwords that hold them. When N * K/32 is
+    // odd the last dword reaches 2 bytes past the last scale; those bytes lie
+    // in the same 16-byte granule as the scale (the array is 16-byte aligned),
+    // hence in a mapped page, and are never used.
+    const sgpr4 sr = raw_rsrc(s, ((uint64_t)N * C * 2 + 3) & ~(uint64_t)3);
+
+    // ---- per-lane copy offsets (the stage enters through the scalar offset)
+    uint32_t xoff[AI];
+#pragma unroll
+    for (int j = 0; j < AI; ++j) {
+        const int r = (w * AI + j) * 8 + (lane >> 3);          // tile row written by this lane
+        const int sl = (lane & 7) ^ ((r >> 1) & 7);            // the logical slot stored at slot lane & 7
+        int m = m0 + r;
+        m = m < M ? m : M - 1;
+        xoff[j] = (uint32_t)m * (uint32_t)K * 2 + (uint32_t)(sl >> 2) * 64 + (uint32_t)(sl & 3) * 16;
+    }
+    const int c = lane & 31, g = lane >> 5;     // column of the tile slice; lane half
+    int ncl = n0 + w * 32 + c;
+    ncl = ncl < N ? ncl : N - 1;
+    // codes: lane (c, g) copies block g of the stage for column c (int8: each of
+    // the two copy instructions moves one 16-byte half of it)
+    const uint32_t qoff = (uint32_t)ncl * qrow + (uint32_t)g * (BITS == 8 ? 32 : 16);
+    const uint32_t hoff = (uint32_t)ncl * qrow + (uint32_t)K / 2 + (uint32_t)g * 4;
+    // scales: lane (c, g) copies the aligned dword holding the scale of block
+    // 2 st + g of column c
+    const uint32_t sidx = (uint32_t)ncl * (uint32_t)C + (uint32_t)g;
+    const uint32_t soff = (sidx * 2) & ~3u;
+
+    // Loads of stage stl into ring buffer `slot`. Issued unconditionally (the
+    // compiler's wait counting then sees the same loads on every path); a stage
+    // past the slice's last re-reads the last one (cache hits), into a buffer
+    // that is never read again.
+    auto issue = [&](int stl, uint8_t *ring) {
+        const int st = st0 + (stl < NTh ? stl : NTh - 1);
+        uint8_t *base = ring + h * SLICE;
+        uint8_t *wb = base + L::A + w * L::WAVE;
+#pragma unroll
+        for (int j = 0; j < AI; ++j) dma16(xr, lds_addr(base + (w * AI + j) * 1024), xoff[j], (uint32_t)st * 128);
+        if constexpr (BITS == 8) {
+            dma16(qr, lds_addr(wb), qoff, (uint32_t)st * 64);
+            dma16(qr, lds_addr(wb + 1024), qoff + 16, (uint32_t)st * 64);
+        } else {
+            dma16(qr, lds_addr(wb), qoff, (uint32_t)st * 32);
+            if constexpr (BITS == 5) dma4(qr, lds_addr(wb + L::BW), hoff, (uint32_t)st * 8);
+        }
+        dma4(sr, lds_addr(wb + L::BW + L::HW), soff, (uint32_t)st * 4);
+    };
+
+    // ---- per-lane read offsets
+    const int t = g ^ ((c >> 1) & 7);           // operand row r = 32 i + c: swizzle (r >> 1) & 7
+    uint32_t aoff[2 * KT];                       // K-step (kb, st): slot 4 kb + 2 st + g, stored at slot ^ swizzle
+#pragma unroll
+    for (int u = 0; u < 2 * KT; ++u) aoff[u] = (uint32_t)c * 128 + (uint32_t)(((2 * u) ^ t) << 4);
+    const uint32_t boff = BITS == 8 ? (uint32_t)(g * 1024 + c * 16) : (uint32_t)(c * 16 + g * 8);
+    // which half of the copied dword holds the scale of block kb of column c
+    const uint32_t scol = (uint32_t)ncl * (uint32_t)C;
+    const int ssh[KT] = {(int)((scol & 1) * 16), (int)(((scol + 1) & 1) * 16)};
     const DecodeConsts dc = DecodeConsts::make();
     Decode5Consts dc5;
     if constexpr (BITS == 5) dc5 = Decode5Consts::make();
-
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)M * K * 4);
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint64_t)N * C * 2);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * K * BITS / 8);
-    const uint32_t qrow = (uint32_t)K * BITS / 8;
-
-    // x: thread t loads XI groups of 8 values: row r, block tb, k-group g.
-    uint32_t xoff[XI];
-    int xblk[XI], xlds[XI];
-#pragma unroll
-    for (int i = 0; i < XI; ++i) {
-        const int idx = t + i * kThreads;        // 0 .. BM*KT*4-1
-        const int r = idx / (KT * 4), sl = idx % (KT * 4);
-        int m = m0 + r;
-        m = m < M ? m : M - 1;
-        xoff[i] = ((uint32_t)m * (uint32_t)K + (uint32_t)(sl & 3) * 8) * 4;
-        xblk[i] = sl >> 2;
-        xlds[i] = aslot(r, sl) * 16;
-    }
-    // scales (and int5 bit-4 dwords): a stage needs KT * BN of them, one per
-    // thread: thread t loads block sk = t % KT of the stage for column t / KT,
-    // so the KT lanes of a column read one cache line. Each lane of such a load
-    // reads a different row of the scales; loading each value once, from as few
-    // lines as possible, measured 10-30% faster than KT loads in every thread.
-    static_assert(kThreads == BN * KT, "one scale per thread and stage");
-    const int sk = t % KT;
-    int sn = n0 + t / KT;
-    sn = sn < N ? sn : N - 1;
-    const uint32_t soff = (uint32_t)sn * (uint32_t)C * 2;
-    // codes: thread t loads QI pieces of 16 bytes; piece pc of a stage is piece
-    // pc % (KT*CB/16) of column pc / (KT*CB/16)'s KT*CB bytes
-    uint32_t qoff[QI];
-    int qblk[QI];
-#pragma unroll
-    for (int i = 0; i < QI; ++i) {
-        const int pc = t + i * kThreads;
-        const int c = pc / (KT * CB / 16);
-        const int k = pc - c * (KT * CB / 16);
-        int n = n0 + c;
-        n = n < N ? n : N - 1;
-        qoff[i] = (uint32_t)n * qrow + (uint32_t)((k * 16) % CB);
-        qblk[i] = (k * 16) / CB;
-    }
-    // one stage's loads in registers; PF sets in flight
-    struct Regs {
-        f4 xv[XI][2];
-        u4 qv[QI];
-        uint16_t sv;                              // scale of block sk of column sn
-        uint32_t hv;                              // int5: its bit-4 dword
-    };
-    Regs rs[PF];
-    const uint32_t hoff = (uint32_t)sn * qrow + (uint32_t)K / 2;
-    // loads of stage st (every address clamped into the tensors, so a stage
-    // past the group's K range loads valid data that is never committed)
-    auto issue = [&](int st, Regs &r) {
-        auto &qv = r.qv;
-        auto &xv = r.xv;
-        auto &sv = r.sv;
-        auto &hv = r.hv;
-        const int b0 = (st0 + st) * KT;
-#pragma unroll
-        for (int i = 0; i < QI; ++i) {
-            int b = b0 + qblk[i];                // blocks past K reload the last one (scale 0)
-            b = b < C ? b : C - 1;
-            qv[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff[i] + (uint32_t)b * CB, 0, 0));
-        }
-#pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            int b = b0 + xblk[i];
-            b = b < C ? b : C - 1;
-            const uint32_t o = xoff[i] + (uint32_t)b * 128;
-            xv[i][0] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0));
-            xv[i][1] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, o + 16, 0, 0));
-        }
-        {
-            const int b = b0 + sk < C ? b0 + sk : C - 1;
-            sv = __builtin_amdgcn_raw_buffer_load_b16(sr, soff + (uint32_t)b * 2, 0, 0);
-            if constexpr (BITS == 5) hv = __builtin_amdgcn_raw_buffer_load_b32(qr, hoff + (uint32_t)b * 4, 0, 0);
-        }
-    };
-    // x rounded to binary16 in operand order, the codes and the scales (zero past
-    // K), into buffer buf
-    auto commit = [&](int st, int buf, const Regs &r) {
-        const auto &qv = r.qv;
-        const auto &xv = r.xv;
-        const auto &sv = r.sv;
-        const auto &hv = r.hv;
-        uint8_t *base = lds + buf * L::BYTES;
-#pragma unroll
-        for (int i = 0; i < QI; ++i) {
-            // piece pc = 16-byte piece k of column c: units 2k and 2k + 1
-            using U = CodeUnits<CB>;
-            const int pc = t + i * kThreads;
-            const int cc = pc / (U::COLB / 16), k = pc - cc * (U::COLB / 16);
-            *reinterpret_cast<u2 *>(base + L::A_BYTES + U::off(cc, 2 * k)) = u2{qv[i].x, qv[i].y};
-            *reinterpret_cast<u2 *>(base + L::A_BYTES + U::off(cc, 2 * k + 1)) = u2{qv[i].z, qv[i].w};
-        }
-#pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const float v[8] = {xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w,
-                                xv[i][1].x, xv[i][1].y, xv[i][1].z, xv[i][1].w};
-            h8 h;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) h[operand_slot<BITS>(k)] = (_Float16)v[k];   // nearest even
-            *reinterpret_cast<h8 *>(base + xlds[i]) = h;
-        }
-        {
-            uint16_t *Sc = reinterpret_cast<uint16_t *>(base + L::A_BYTES + L::B_BYTES + L::H_BYTES);
-            const int b = (st0 + st) * KT + sk;
-            Sc[t] = b < C ? sv : (uint16_t)0;    // column t / KT, block sk
-            if constexpr (BITS == 5) {
-                uint32_t *H = reinterpret_cast<uint32_t *>(base + L::A_BYTES + L::B_BYTES);
-                H[t] = hv;
-            }
-        }
-    };
 
     f16v acc[RF];
 #pragma unroll
     for (int i = 0; i < RF; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-
     const f16v zero = {};
-    const int c = wave * 32 + (lane & 31);       // this lane's column of the tile
-    const int g = lane >> 5;                     // its k-group within a K-step of 16
-    // the matrix work of stage it, from LDS buffer it & 1
-    auto compute = [&](int it) {
-        const int cur = it & 1;
-        const uint8_t *base = lds + cur * L::BYTES;
-        const uint8_t *B = base + L::A_BYTES;
-        const uint8_t *H = B + L::B_BYTES;
-        const uint16_t *Sc = reinterpret_cast<const uint16_t *>(H + L::H_BYTES);
-        // A fragments one K-step ahead (K-step q of the stage is at slot 2q + g)
-        h8 acur[RF];
-#pragma unroll
-        for (int i = 0; i < RF; ++i) acur[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), g) * 16);
-        // the stage's code words and scales of this lane, read together at the
-        // stage start (one LDS wait for the whole stage)
-        using U = CodeUnits<CB>;
-        u2 cw[KT][2];
-        uint32_t hbs[KT][2];
-        uint16_t scb[KT];
+
+    auto compute = [&](int stl, const uint8_t *ring) {
+        const int st = st0 + stl;
+        const uint8_t *A = ring + h * SLICE;
+        const uint8_t *wb = A + L::A + w * L::WAVE;
 #pragma unroll
         for (int kb = 0; kb < KT; ++kb) {
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                if constexpr (BITS == 8) {
-                    cw[kb][st] = *reinterpret_cast<const u2 *>(B + U::off(c, 4 * kb + 2 * st + g));
+            h8 b[2];
+            if constexpr (BITS == 8) {
+                const u4 cw = *reinterpret_cast<const u4 *>(wb + kb * 512 + boff);
+                b[0] = unpack8_int8(cw.x, cw.y, dc);
+                b[1] = unpack8_int8(cw.z, cw.w, dc);
+            } else {
+                const u2 cw = *reinterpret_cast<const u2 *>(wb + kb * 512 + boff);
+                if constexpr (BITS == 5) {
+                    const uint32_t hb = *reinterpret_cast<const uint32_t *>(wb + L::BW + (kb * 32 + c) * 4) >> (16 * g);
+                    b[0] = unpack8_int5(cw.x, hb & 0xFFu, dc5);
+                    b[1] = unpack8_int5(cw.y, (hb >> 8) & 0xFFu, dc5);
                 } else {
-                    cw[kb][st].x = *reinterpret_cast<const uint32_t *>(B + U::off(c, 2 * kb + st) + g * 4);
-                    if constexpr (BITS == 5) hbs[kb][st] = H[(c * KT + kb) * 4 + 2 * st + g];
+                    b[0] = unpack8_int4(cw.x, dc);
+                    b[1] = unpack8_int4(cw.y, dc);
                 }
             }
-            scb[kb] = Sc[c * KT + kb];
-        }
+            const uint32_t sw = *reinterpret_cast<const uint32_t *>(wb + L::BW + L::HW + (kb * 32 + c) * 4);
+            float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> ssh[kb]));
+            sc = (st * KT + kb < C) ? sc : 0.0f;      // blocks past K contribute nothing
+            asm volatile("" : "+v"(sc));
+            h8 a0[RF], a1[RF];
 #pragma unroll
-        for (int kb = 0; kb < KT; ++kb) {
-            // this lane's 8 codes of each K-step (k = 16*st + 8*g .. +7 of block kb),
-            // unpacked once and used by every row fragment
-            h8 b[2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                if constexpr (BITS == 4) b[st] = unpack8_int4(cw[kb][st].x, dc);
-                else if constexpr (BITS == 5) b[st] = unpack8_int5(cw[kb][st].x, hbs[kb][st], dc5);
-                else b[st] = unpack8_int8(cw[kb][st].x, cw[kb][st].y, dc);
+            for (int i = 0; i < RF; ++i) {
+                a0[i] = *reinterpret_cast<const h8 *>(A + aoff[2 * kb] + i * 4096);
+                a1[i] = *reinterpret_cast<const h8 *>(A + aoff[2 * kb + 1] + i * 4096);
             }
-            float sc = (float)__builtin_bit_cast(_Float16, scb[kb]);
-            asm volatile("" : "+v"(sc));             // fp32 scale: plain FMAs
-            // block partial of every row fragment: two chained K-steps of 16
             f16v p[RF];
-            h8 anx[RF];
 #pragma unroll
-            for (int i = 0; i < RF; ++i) anx[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), kb * 4 + 2 + g) * 16);
+            for (int i = 0; i < RF; ++i) p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[i], b[0], zero, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < RF; ++i) p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[i], b[0], zero, 0, 0, 0);
-            if (kb + 1 < KT) {
-#pragma unroll
-                for (int i = 0; i < RF; ++i) acur[i] = *reinterpret_cast<const h8 *>(base + aslot(i * 32 + (lane & 31), (kb + 1) * 4 + g) * 16);
-            }
-#pragma unroll
-            for (int i = 0; i < RF; ++i) p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(anx[i], b[1], p[i], 0, 0, 0);
-            // acc += scale * partial, block by block; the matrix work of other
-            // wavefronts runs meanwhile
+            for (int i = 0; i < RF; ++i) p[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[i], b[1], p[i], 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < RF; ++i) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][v] = __builtin_fmaf(sc, p[i][v], acc[i][v]);
-                asm volatile("" : "+v"(acc[i]));    // the scaling happens here
             }
         }
     };
 
-    if constexpr (PF == 1) {
-        issue(0, rs[0]);
-        commit(0, 0, rs[0]);                     // waits for stage 0's loads
-        __syncthreads();
-        if (NTh > 1) issue(1, rs[0]);
-        for (int it = 0; it < NTh; ++it) {
-            compute(it);
-            if (it + 1 < NTh) {
-                commit(it + 1, (it + 1) & 1, rs[0]);   // waits for stage it+1's loads
-                __syncthreads();                 // every wave is done with buffer it & 1
-                if (it + 2 < NTh) issue(it + 2, rs[0]);
-            }
+    // Stage stl (in ring buffer `slot`): wait for this wavefront's loads of it
+    // (exactly NS - 2 later stages are in flight behind it), barrier (everyone's
+    // copies have landed and everyone is done with the buffer about to be
+    // refilled), refill that buffer (`nxt`) with stage stl + NS - 1, compute.
+    auto step = [&](int stl, const uint8_t *cur, uint8_t *nxt) {
+        wait_vm<V * (NS - 2)>();
+        lds_barrier();
+        issue(stl + NS - 1, nxt);
+        compute(stl, cur);
+    };
+
+    issue(0, ring0);
+    if constexpr (NS >= 3) issue(1, ring1);
+    if constexpr (NS >= 4) issue(2, ring2);
+    int sb = 0;
+    for (; sb + NS <= NTh; sb += NS) {
+        if constexpr (NS == 2) {
+            step(sb, ring0, ring1);
+            step(sb + 1, ring1, ring0);
+        } else if constexpr (NS == 3) {
+            step(sb, ring0, ring2);
+            step(sb + 1, ring1, ring0);
+            step(sb + 2, ring2, ring1);
+        } else {
+            step(sb, ring0, ring3);
+            step(sb + 1, ring1, ring0);
+            step(sb + 2, ring2, ring1);
+            step(sb + 3, ring3, ring2);
         }
-    } else {
-        // stage j's loads go to register set j % 2, issued two stages ahead, always
-        // (no load under a branch, so each commit waits only for its own set)
-        static_assert(PF == 2, "prefetch depth 1 or 2");
-        issue(0, rs[0]);
-        issue(1, rs[1]);
-        commit(0, 0, rs[0]);                     // waits for stage 0's loads only
-        __syncthreads();
-        issue(2, rs[0]);
-        int it = 0;
-        for (; it + 1 < NTh; it += 2) {
-            compute(it);
-            commit(it + 1, 1, rs[1]);
-            __syncthreads();
-            issue(it + 3, rs[1]);
-            compute(it + 1);
-            if (it + 2 < NTh) {
-                commit(it + 2, 0, rs[0]);
-                __syncthreads();
-            }
-            issue(it + 4, rs[0]);
-        }
-        if (it < NTh) compute(it);
     }
-    if constexpr (S > 1) {
-        // groups 1..S-1 hand their partial sums to group 0 through LDS, which
-        // adds them in group order (a fixed order: results are deterministic)
-        float *red = reinterpret_cast<float *>(lds_all);
-        __syncthreads();                         // every group is done with its buffers
-        if (h > 0) {
+    if (sb < NTh) step(sb, ring0, NS == 2 ? ring1 : (NS == 3 ? ring2 : ring3));
+    if (NS >= 3 && sb + 1 < NTh) step(sb + 1, ring1, ring0);
+    if (NS >= 4 && sb + 2 < NTh) step(sb + 2, ring2, ring1);
+    // the copies of the stages past the end are still in flight: let them land
+    // before the LDS is reused or released
+    wait_vm<0>();
+    lds_barrier();
+
+    if constexpr (SK > 1) {
+        // slices 1..SK-1 hand their partial sums to slice 0 through LDS, one
+        // fragment at a time, in slice order (a fixed order: deterministic)
+        float *red = reinterpret_cast<float *>(ring0);
+        static_assert(WN * 64 * 16 * 4 <= SK * T::SLICE, "reduction buffer");
 #pragma unroll
-            for (int i = 0; i < RF; ++i)
+        for (int j = 1; j < SK; ++j) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) red[(((h - 1) * RF + i) * 16 + v) * kThreads + t] = acc[i][v];
+            for (int i = 0; i < RF; ++i) {
+                lds_barrier();
+                if (h == j) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) red[(v * WN + w) * 64 + lane] = acc[i][v];
+                }
+                lds_barrier();
+                if (h == 0) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][v] += red[(v * WN + w) * 64 + lane];
+                }
+            }
         }
-        __syncthreads();
         if (h > 0) return;
-#pragma unroll
-        for (int j = 1; j < S; ++j)
-#pragma unroll
-            for (int i = 0; i < RF; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][v] += red[(((j - 1) * RF + i) * 16 + v) * kThreads + t];
     }
 
     // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
-    // column l%32.
-    const int n = n0 + c;
-    if (m0 + BM <= M && n0 + BN <= N) {
-        // a whole tile: no per-value bounds checks (no branches between the stores)
-        float *yp = y + (size_t)(m0 + 4 * g) * N + n;
+    // column l%32; y = acc * 2^-e_m.
+    // the factors' region is padded to 256 bytes, so the 4-row loads of rows < M
+    // stay inside it (rows >= M are loaded but never stored)
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rinv, gemm_ws_rinv_bytes(M));
+    const int n = n0 + w * 32 + c;
+    const bool whole = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-        for (int i = 0; i < RF; ++i)
+    for (int i = 0; i < RF; ++i) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                __builtin_nontemporal_store(acc[i][v], yp + (size_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * N);
-    } else {
+        for (int j = 0; j < 4; ++j) {
+            const int mr = m0 + i * 32 + 8 * j + 4 * g;               // rows mr .. mr+3
+            const f4 f = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)mr * 4, 0, 0));
+            const float fv[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-        for (int i = 0; i < RF; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-                if (m < M && n < N) __builtin_nontemporal_store(acc[i][v], y + (size_t)m * N + n);
+            for (int u = 0; u < 4; ++u) {
+                const float val = acc[i][4 * j + u] * fv[u];
+                if (whole) {
+                    __builtin_nontemporal_store(val, y + (size_t)(mr + u) * N + n);
+                } else if (mr + u < M && n < N) {
+                    __builtin_nontemporal_store(val, y + (size_t)(mr + u) * N + n);
+                }
             }
+        }
     }
 }
 
-template <int BITS, int BM, int S>
-__global__ WQ_GEMM_BOUNDS(S) void gemm_kernel(const float *__restrict__ x, int M, int K, int N,
-                                             const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
-                                             float *__restrict__ y, int tiles_m, int tiles_n)
+template <int BITS, int BM, int WN, int SK, int NS>
+__global__ WQ_GEMM_BOUNDS(WN, SK) void gemm_kernel(const _Float16 *__restrict__ x16, const float *__restrict__ rinv,
+                                                    int M, int K, int N, const uint8_t *__restrict__ q,
+                                                    const uint16_t *__restrict__ s, float *__restrict__ y,
+                                                    int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_all[S * 2 * Stage<BITS, BM>::BYTES];
+    constexpr int SZ = SK * Tile<BITS, BM, WN, SK, NS>::SLICE;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[SZ];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[SZ];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS >= 3 ? SZ : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS >= 4 ? SZ : 16];
     // XCD-aware tile order: workgroups id, id+8, id+16, ... run on one XCD; give
     // them consecutive tiles (row-major over (tm, tn)).
     const int T = tiles_m * tiles_n;
@@ -410,7 +473,8 @@ __global__ WQ_GEMM_BOUNDS(S) void gemm_kernel(const float *__restrict__ x, int M
     const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (tile >= T) return;
     const int tm = tile / tiles_n;
-    gemm_tile<BITS, BM, S>(x, M, K, N, q, s, y, tm, tile - tm * tiles_n, lds_all);
+    gemm_tile<BITS, BM, WN, SK, NS>(x16, rinv, M, K, N, q, s, y, tm, tile - tm * tiles_n, ring0, ring1, ring2,
+                                    ring3);
 }
 
 // Grouped prefill: the work items of every tensor of a planned table in one
@@ -418,19 +482,22 @@ __global__ WQ_GEMM_BOUNDS(S) void gemm_kernel(const float *__restrict__ x, int M
 // holds it; within an entry, item j is tile (j % tiles_m, j / tiles_m), so with
 // entries starting at multiples of 8 the items of one XCD (i % 8) share row
 // tiles of x. Items past an entry's tiles (alignment padding) do nothing.
-template <int BM, int S>
-__global__ WQ_GEMM_BOUNDS(S) void gemm_grouped_kernel(const uint8_t *__restrict__ base,
-                                                      const wq_desc *__restrict__ table, int count, int M)
+template <int BM, int WN, int SK, int NS>
+__global__ WQ_GEMM_BOUNDS(WN, SK) void gemm_grouped_kernel(const uint8_t *__restrict__ base,
+                                                           const wq_desc *__restrict__ table, int count, int M,
+                                                           const uint8_t *__restrict__ ws)
 {
-    // int8 has the largest stage of the three code widths
-    static_assert(Stage<8, BM>::BYTES >= Stage<4, BM>::BYTES && Stage<8, BM>::BYTES >= Stage<5, BM>::BYTES, "");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_all[S * 2 * Stage<8, BM>::BYTES];
+    constexpr int SZ = SK * Tile<8, BM, WN, SK, NS>::SLICE;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[SZ];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[SZ];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS >= 3 ? SZ : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS >= 4 ? SZ : 16];
     const int64_t item = blockIdx.x;
     const int tiles_m = (M + BM - 1) / BM;
     int e = -1;
     for (int i = 0; i < count; ++i) {
         const int64_t tb = table[i].tile_begin;
-        const int64_t tiles = (int64_t)tiles_m * ((table[i].N + BN - 1) / BN);
+        const int64_t tiles = (int64_t)tiles_m * ((table[i].N + 32 * WN - 1) / (32 * WN));
         if (item >= tb && item < tb + tiles) { e = i; break; }
     }
     if (e < 0) return;
@@ -440,78 +507,89 @@ __global__ WQ_GEMM_BOUNDS(S) void gemm_grouped_kernel(const uint8_t *__restrict_
     const int K = (int)d.K, N = (int)d.N;
     const uint8_t *q = base + d.q_off;
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(base + d.s_off);
-    if (d.bits == 4) gemm_tile<4, BM, S>(d.x, M, K, N, q, sc, d.y, tm, tn, lds_all);
-    else if (d.bits == 5) gemm_tile<5, BM, S>(d.x, M, K, N, q, sc, d.y, tm, tn, lds_all);
-    else gemm_tile<8, BM, S>(d.x, M, K, N, q, sc, d.y, tm, tn, lds_all);
+    const uint8_t *slot = ws + (size_t)d.ws_slot * kGemmWsUnit;
+    const _Float16 *x16 = reinterpret_cast<const _Float16 *>(slot);
+    const float *rinv = reinterpret_cast<const float *>(slot + gemm_ws_x16_bytes(M, K));
+    if (d.bits == 4)
+        gemm_tile<4, BM, WN, SK, NS>(x16, rinv, M, K, N, q, sc, d.y, tm, tn, ring0, ring1, ring2, ring3);
+    else if (d.bits == 5)
+        gemm_tile<5, BM, WN, SK, NS>(x16, rinv, M, K, N, q, sc, d.y, tm, tn, ring0, ring1, ring2, ring3);
+    else
+        gemm_tile<8, BM, WN, SK, NS>(x16, rinv, M, K, N, q, sc, d.y, tm, tn, ring0, ring1, ring2, ring3);
 }
 
-template <int BITS, int BM, int S>
-hipError_t launch_bits(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
-                       const uint16_t *scales, float *y, hipStream_t stream)
+template <int BITS, int BM, int WN, int SK, int NS>
+hipError_t launch_cfg(const _Float16 *x16, const float *rinv, int64_t M, int64_t K, int64_t N, const void *q,
+                      const uint16_t *scales, float *y, hipStream_t stream)
 {
     const int tiles_m = (int)((M + BM - 1) / BM);
-    const int tiles_n = (int)((N + BN - 1) / BN);
+    const int tiles_n = (int)((N + 32 * WN - 1) / (32 * WN));
     const int T = tiles_m * tiles_n;
     const unsigned grid = (unsigned)(((T + kXcds - 1) / kXcds) * kXcds);
-    gemm_kernel<BITS, BM, S><<<grid, kThreads * S, 0, stream>>>(x, (int)M, (int)K, (int)N, (const uint8_t *)q,
-                                                                scales, y, tiles_m, tiles_n);
+    gemm_kernel<BITS, BM, WN, SK, NS><<<grid, WN * SK * 64, 0, stream>>>(
+        x16, rinv, (int)M, (int)K, (int)N, (const uint8_t *)q, scales, y, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-// Tile height and K split. With at least 256 tiles of 128 x 128 (M >= 256),
-// 128-row tiles: each unpacked code feeds four row fragments (measured 3-9%
-// faster than 64 rows at M = 4096); with fewer than 512 of them (under two per
-// compute unit) the K loop of each is split over 2 groups (the M = 4096 down
-// projection: 9% faster; splitting 768 tiles was 10% slower). Else with at
-// least 256 tiles of 64 x 128,
-// 64-row tiles; fewer: 32-row tiles with the K loop of each tile split over 4
-// groups (2 when it has fewer than 4 stages), so every SIMD runs several
-// wavefronts; the time of a tile is then about a quarter of its serial K loop.
+// Tile shape, K split and ring depth of a single call:
+//  - long prefills (at least 512 tiles of 128 x 128): 128-row tiles, each code
+//    unpack feeding four row fragments, three stages in flight, two
+//    workgroups per compute unit;
+//  - 256..511 such tiles: the same tiles with the K loop split over two
+//    wavefront groups of one workgroup;
+//  - fewer: 64-row tiles (the M = 64 int8 lm_head has 1187 of them) with four
+//    stages in flight, or for few of those, 64-row tiles with a two-way split.
 template <int BITS>
-hipError_t launch_shape(const float *x, int64_t M, int64_t K, int64_t N, const void *q,
+hipError_t launch_shape(const _Float16 *x16, const float *rinv, int64_t M, int64_t K, int64_t N, const void *q,
                         const uint16_t *scales, float *y, hipStream_t stream)
 {
-    const int64_t tn = (N + BN - 1) / BN;
-    const int64_t stages = (K / 32 + KT - 1) / KT;
+    const int64_t tn = (N + 127) / 128;
     const int64_t t128 = ((M + 127) / 128) * tn;
-    if (M >= 256 && t128 >= 256) {
-        // fewer than two tiles per compute unit: split each tile's K loop in two
-        if (t128 < 512) return launch_bits<BITS, 128, 2>(x, M, K, N, q, scales, y, stream);
-        return launch_bits<BITS, 128, 1>(x, M, K, N, q, scales, y, stream);
-    }
-    if (((M + 63) / 64) * tn >= 256 || stages < 2) return launch_bits<BITS, 64, 1>(x, M, K, N, q, scales, y, stream);
-    if (stages < 4) return launch_bits<BITS, 32, 2>(x, M, K, N, q, scales, y, stream);
-    return launch_bits<BITS, 32, 4>(x, M, K, N, q, scales, y, stream);
+    const int64_t t64 = ((M + 63) / 64) * tn;
+    if (M > 64 && t128 >= 512) return launch_cfg<BITS, 128, 4, 1, 3>(x16, rinv, M, K, N, q, scales, y, stream);
+    if (M > 64 && t128 >= 256) return launch_cfg<BITS, 128, 4, 2, 3>(x16, rinv, M, K, N, q, scales, y, stream);
+    if (t64 >= 256) return launch_cfg<BITS, 64, 4, 1, 4>(x16, rinv, M, K, N, q, scales, y, stream);
+    return launch_cfg<BITS, 64, 4, 2, 3>(x16, rinv, M, K, N, q, scales, y, stream);
 }
 
-template <int BM, int S>
+template <int BM, int WN, int SK, int NS>
 hipError_t launch_grouped(const void *base, const wq_desc *table, int count, int64_t total_tiles, int64_t M,
-                          hipStream_t stream)
+                          const void *ws, hipStream_t stream)
 {
-    gemm_grouped_kernel<BM, S><<<(unsigned)total_tiles, kThreads * S, 0, stream>>>(
-        (const uint8_t *)base, table, count, (int)M);
+    gemm_grouped_kernel<BM, WN, SK, NS><<<(unsigned)total_tiles, WN * SK * 64, 0, stream>>>(
+        (const uint8_t *)base, table, count, (int)M, (const uint8_t *)ws);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_grouped(const void *base, const wq_desc *table, int count, int64_t total_tiles,
-                               int64_t M, hipStream_t stream)
+hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
+                       const uint16_t *scales, float *y, void *ws, hipStream_t stream)
 {
-    static_assert(BN == kGemmTileN, "tile width");
-    const int bm = gemm_grouped_bm(M), sp = gemm_grouped_split(M);
-    if (bm == 32 && sp == 4) return launch_grouped<32, 4>(base, table, count, total_tiles, M, stream);
-    if (bm == 64 && sp == 1) return launch_grouped<64, 1>(base, table, count, total_tiles, M, stream);
-    if (bm == 128 && sp == 1) return launch_grouped<128, 1>(base, table, count, total_tiles, M, stream);
-    return hipErrorInvalidValue;
+    _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
+    float *rinv = reinterpret_cast<float *>((uint8_t *)ws + gemm_ws_x16_bytes(M, K));
+    const unsigned pgrid = (unsigned)((M + 3) / 4);
+    if (bits == 8) xprep_kernel<1><<<pgrid, 256, 0, stream>>>(x, (int)M, (int)K, x16, rinv);
+    else xprep_kernel<0><<<pgrid, 256, 0, stream>>>(x, (int)M, (int)K, x16, rinv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (bits == 4) return launch_shape<4>(x16, rinv, M, K, N, q, scales, y, stream);
+    if (bits == 5) return launch_shape<5>(x16, rinv, M, K, N, q, scales, y, stream);
+    return launch_shape<8>(x16, rinv, M, K, N, q, scales, y, stream);
 }
 
-hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
-                       const uint16_t *scales, float *y, hipStream_t stream)
+hipError_t launch_gemm_grouped(const void *base, const wq_desc *table, int count, int64_t total_tiles, int64_t M,
+                               void *ws, hipStream_t stream)
 {
-    if (bits == 4) return launch_shape<4>(x, M, K, N, q, scales, y, stream);
-    if (bits == 5) return launch_shape<5>(x, M, K, N, q, scales, y, stream);
-    return launch_shape<8>(x, M, K, N, q, scales, y, stream);
+    static_assert(kGemmTileN == 128, "tile width of every grouped shape");
+    dim3 pgrid((unsigned)((M + 3) / 4), (unsigned)count);
+    xprep_grouped_kernel<<<pgrid, 256, 0, stream>>>(table, count, (int)M, (uint8_t *)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int bm = gemm_grouped_bm(M), sp = gemm_grouped_split(M);
+    if (bm == 64 && sp == 2) return launch_grouped<64, 4, 2, 3>(base, table, count, total_tiles, M, ws, stream);
+    if (bm == 128 && sp == 1) return launch_grouped<128, 4, 1, 3>(base, table, count, total_tiles, M, ws, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace wq

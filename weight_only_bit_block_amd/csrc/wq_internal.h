@@ -126,16 +126,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint6
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)(uint32_t)bytes, 0x00020000);
 }
 
+// ---------------------------------------------------------------- prefill workspace
+// The prefill GEMM rounds x to binary16 once per call (after a per-row
+// power-of-two normalisation) into a workspace: the prepared x [M][K]
+// (binary16), then the per-row factors 2^-e [M] (fp32), each region padded to
+// 256 bytes. A grouped call holds one such slot per distinct (x, code order),
+// at a multiple of 256 bytes (wq_desc.ws_slot, in 256-byte units).
+constexpr uint64_t kGemmWsUnit = 256;
+__host__ __device__ inline uint64_t gemm_ws_round(uint64_t b) { return (b + kGemmWsUnit - 1) / kGemmWsUnit * kGemmWsUnit; }
+__host__ __device__ inline uint64_t gemm_ws_x16_bytes(int64_t M, int64_t K) { return gemm_ws_round((uint64_t)M * (uint64_t)K * 2); }
+__host__ __device__ inline uint64_t gemm_ws_rinv_bytes(int64_t M) { return gemm_ws_round((uint64_t)M * 4); }
+__host__ __device__ inline uint64_t gemm_ws_bytes(int64_t M, int64_t K) { return gemm_ws_x16_bytes(M, K) + gemm_ws_rinv_bytes(M); }
+
 // ---------------------------------------------------------------- grouped prefill geometry
 // A grouped prefill launch uses one tile shape for every tensor, chosen by M
 // alone: BM-row x 128-column tiles, with the K loop of each tile split over S
-// groups of 256 threads. Short prefills (M <= 128) take 32-row tiles split 4
-// ways (measured 14% faster than 2 ways and 24% faster than unsplit for the
-// seven projections of a layer at M = 128); longer ones 64 or 128 rows, unsplit.
+// groups of 256 threads. Short prefills (M <= 128) take 64-row tiles split
+// two ways; longer ones 128-row tiles, unsplit.
 constexpr int kGemmTileN = 128;
 constexpr int kGemmGroupAlign = 8;  // entries start at multiples of 8 items (one per XCD)
-inline int gemm_grouped_bm(int64_t M) { return M <= 128 ? 32 : (M <= 512 ? 64 : 128); }
-inline int gemm_grouped_split(int64_t M) { return gemm_grouped_bm(M) == 32 ? 4 : 1; }
+inline int gemm_grouped_bm(int64_t M) { return M <= 128 ? 64 : 128; }
+inline int gemm_grouped_split(int64_t M) { return gemm_grouped_bm(M) == 64 ? 2 : 1; }
 inline int64_t gemm_grouped_items(int64_t M, int64_t N)
 {
     const int bm = gemm_grouped_bm(M);
@@ -151,10 +162,11 @@ hipError_t launch_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits
                        const void *q, const uint16_t *scales, float *y, hipStream_t stream);
 hipError_t launch_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
                                int64_t total_tiles, int64_t M, hipStream_t stream);
+// ws: gemm_ws_bytes(M, K) bytes (single call) or the planned workspace (grouped)
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
-                       const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+                       const void *q, const uint16_t *scales, float *y, void *ws, hipStream_t stream);
 hipError_t launch_gemm_grouped(const void *base, const wq_desc *table_dev, int count,
-                               int64_t total_tiles, int64_t M, hipStream_t stream);
+                               int64_t total_tiles, int64_t M, void *ws, hipStream_t stream);
 hipError_t launch_mgemv(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                         const uint16_t *scales, float *y, hipStream_t stream);
 hipError_t launch_mgemv_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_items,

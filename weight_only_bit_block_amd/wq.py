@@ -34,7 +34,7 @@ class WqDesc(ctypes.Structure):
     """Mirror of `struct wq_desc` (64 bytes)."""
     _fields_ = [
         ("bits", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("ws_slot", ctypes.c_int32),
         ("N", ctypes.c_int64),
         ("K", ctypes.c_int64),
         ("q_off", ctypes.c_uint64),
@@ -69,9 +69,9 @@ def load(path: Optional[str] = None):
         getattr(lib, f).argtypes = mm
     lib.wq_table_layout.argtypes = [P, I, ctypes.POINTER(ctypes.c_uint64)]
     lib.wq_table_plan.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64)]
-    lib.wq_table_plan_gemm.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64)]
+    lib.wq_table_plan_gemm.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64)]
     lib.wq_gemv_grouped.argtypes = [P, P, I, I64, I64, P]
-    lib.wq_gemm_grouped.argtypes = [P, P, I, I64, I64, P]
+    lib.wq_gemm_grouped.argtypes = [P, P, I, I64, I64, P, ctypes.c_uint64, P]
     lib.wq_embed.argtypes = [P, I64, I64, I64, I, P, P, P, P]
     lib.wq_strerror.argtypes = [I]
     lib.wq_strerror.restype = ctypes.c_char_p
@@ -247,12 +247,14 @@ def table_plan(arr, M: int) -> int:
     return int(total.value)
 
 
-def table_plan_gemm(arr, M: int) -> int:
-    """Set tile_begin for a grouped prefill call with M rows; returns the launch size."""
+def table_plan_gemm(arr, M: int) -> Tuple[int, int]:
+    """Set tile_begin and ws_slot for a grouped prefill call with M rows;
+    returns (launch size, workspace bytes)."""
     total = ctypes.c_int64(0)
+    ws = ctypes.c_uint64(0)
     _check(load().wq_table_plan_gemm(ctypes.addressof(arr) if len(arr) else None, len(arr), M,
-                                     ctypes.byref(total)), "wq_table_plan_gemm")
-    return int(total.value)
+                                     ctypes.byref(total), ctypes.byref(ws)), "wq_table_plan_gemm")
+    return int(total.value), int(ws.value)
 
 
 class Package:
@@ -306,7 +308,14 @@ class GroupedCall:
             _need(tuple(x.shape) == (M, K) and tuple(y.shape) == (M, N), f"tensor {i}: x/y shape")
             arr[i].x, arr[i].y = _ptr(x), _ptr(y)
         self.prefill = prefill
-        self.total_tiles = table_plan_gemm(arr, M) if prefill else table_plan(arr, M)
+        self.ws_bytes = 0
+        if prefill:
+            self.total_tiles, self.ws_bytes = table_plan_gemm(arr, M)
+        else:
+            self.total_tiles = table_plan(arr, M)
+        # the prefill workspace (prepared x per distinct input), 256-byte aligned
+        self._wsbuf = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
+        self.ws = _ptr(self._wsbuf) + (-_ptr(self._wsbuf)) % 256
         self.M = M
         self.count = len(pkg.specs)
         self.pkg = pkg
@@ -319,6 +328,9 @@ class GroupedCall:
         self.keep = (list(xs), list(ys))
 
     def __call__(self, stream=None):
-        fn = "wq_gemm_grouped" if self.prefill else "wq_gemv_grouped"
-        _check(getattr(load(), fn)(self.pkg.base, _ptr(self.table_dev), self.count,
-                                   self.total_tiles, self.M, _stream(stream)), fn)
+        if self.prefill:
+            _check(load().wq_gemm_grouped(self.pkg.base, _ptr(self.table_dev), self.count, self.total_tiles,
+                                          self.M, self.ws, self.ws_bytes, _stream(stream)), "wq_gemm_grouped")
+        else:
+            _check(load().wq_gemv_grouped(self.pkg.base, _ptr(self.table_dev), self.count,
+                                          self.total_tiles, self.M, _stream(stream)), "wq_gemv_grouped")
