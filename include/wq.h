@@ -26,11 +26,12 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers on the current HIP device, owned by the
- *     caller. The library keeps no state besides one device memory pool per
- *     device, from which wq_gemm (and wq_linear for M > 16) takes its
- *     workspace with stream-ordered allocation on the caller's stream (created
- *     on first use, kept until the process ends); no other entry point
- *     allocates.
+ *     caller. The only state the library keeps is the workspace of wq_gemm
+ *     (and wq_linear for M > 16): one stream-ordered device memory pool per
+ *     device (created on first use, kept until the process ends) and, per
+ *     (device, stream), the workspace of the last call on that stream, reused
+ *     while large enough (calls on one stream run in order; streams are told
+ *     apart by their process-unique id). No other entry point allocates.
  *   - Arguments are validated on the host before any launch; a non-zero
  *     wq_status is returned and nothing is launched. Requirements: bits in
  *     {4, 5, 8}; K > 0 and K % 32 == 0 (K % 128 == 0 for int5, so rows stay
@@ -122,15 +123,16 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
  *      each 32-wide K step is one quantization block, computed by fp16
  *      matrix-core instructions into an fp32 partial that is scaled by that
  *      block's scale and accumulated in fp32; y = acc * 2^-e_m.
- * The workspace (about 2*M*K bytes) comes from the library's stream-ordered
- * pool on the current device and is released on `stream` after the launch.
+ * The workspace (about 2*M*K bytes) is the calling stream's buffer from the
+ * library's pool on the current device (grown when too small; a fresh pool
+ * allocation, freed inside the capture, while the stream is being captured).
  * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call for finite x whose
  * rows' largest magnitudes are at least 2^-112 (values below 2^-28 of their
  * row's largest magnitude are rounded with an absolute error under 2^-39 of
  * it). A row holding inf or NaN gives non-finite outputs in that row only.
- * Sizes: M * K * 2, N * K * bits / 8 and N * K / 16 must each be below 2^32
- * (32-bit offsets in the kernels), else WQ_ERR_SHAPE. A pool allocation
- * failure is reported as WQ_ERR_HIP.
+ * Sizes: M * K * 2, N * K * bits / 8 and N * K / 16 must each be below 2^32,
+ * and N below 2^22 (32-bit offsets in the kernels), else WQ_ERR_SHAPE. A pool
+ * allocation failure is reported as WQ_ERR_HIP.
  */
 int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
             const void *q, const uint16_t *scales, float *y, hipStream_t stream);
@@ -205,7 +207,7 @@ int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
  * wq_table_plan_gemm -- host only. For a grouped prefill call (wq_gemm_grouped)
  * with M >= 1 rows, set tile_begin and ws_slot of every entry, return the
  * launch size in *total_tiles and the workspace size in *workspace_bytes.
- * Validates every entry as wq_table_plan does, and M * K * 2 < 2^32 for each.
+ * Validates every entry as wq_table_plan does, and wq_gemm's size limits for each.
  * Work items are dispatched longest K first (ties in table order), and each
  * entry's items start at a multiple of 8. Entries that read the same x (same
  * pointer and K) with the same code order (int8, or int4/int5) share one

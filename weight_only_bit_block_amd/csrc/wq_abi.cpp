@@ -4,7 +4,8 @@
 // Every check runs on the host before anything is launched; a failing check
 // returns a status and touches no HIP state. Launches go to the caller's
 // stream; nothing is synchronized here. The only allocation is the prefill
-// workspace of wq_gemm, taken from a per-device stream-ordered memory pool.
+// workspace of wq_gemm (a per-(device, stream) buffer from a stream-ordered
+// memory pool, reused across calls).
 #include <stdint.h>
 #include <string.h>
 
@@ -14,44 +15,112 @@
 
 namespace {
 
-// ---------------------------------------------------------------- workspace pool
-// One pool per device, created on first use and kept until the process ends
-// (its release threshold is the maximum, so freed blocks stay in the pool and
-// later calls on any stream reuse them without returning to the driver).
+// ---------------------------------------------------------------- workspace
+// One stream-ordered memory pool per device, created on first use and kept
+// until the process ends (its release threshold is the maximum, so freed
+// blocks stay in the pool). On top of it, each (device, stream handle) keeps
+// the workspace of its last prefill call and reuses it while it is large
+// enough. Each buffer carries an event recorded after its last use; a call
+// makes its stream wait for that event before using the buffer, so two uses
+// never overlap even when a stream handle is reused after a stream was
+// destroyed with work still pending. A larger need replaces the buffer (the
+// old one is freed on the stream of its last use, after that work); with more
+// streams than cache entries the least recently used entry is released the
+// same way. Calls made while the stream is being captured into a graph take a
+// fresh pool allocation, freed inside the capture.
 constexpr int kMaxDevices = 64;
-std::mutex g_pool_mu;
+constexpr int kWsEntries = 16;
+std::mutex g_ws_mu;
 hipMemPool_t g_pools[kMaxDevices] = {};
 
-hipError_t pool_alloc(void **p, size_t bytes, hipStream_t stream)
+struct WsEntry {
+    int dev;
+    hipStream_t stream;      // stream of the last use
+    void *ptr;
+    size_t bytes;
+    hipEvent_t done;         // recorded on `stream` after the last use
+    uint64_t last;
+};
+WsEntry g_ws[kWsEntries] = {};
+uint64_t g_ws_clock = 0;
+
+// The device's pool (g_ws_mu held).
+hipError_t device_pool(int dev, hipMemPool_t *out)
 {
+    if (!g_pools[dev]) {
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof props);
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t created = nullptr;
+        hipError_t e = hipMemPoolCreate(&created, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(created);
+            return e;
+        }
+        g_pools[dev] = created;
+    }
+    *out = g_pools[dev];
+    return hipSuccess;
+}
+
+// A workspace of at least `bytes` for work on `stream`. *entry is set for a
+// cached buffer (the caller records its event after the launches) and null for
+// a fresh allocation the caller frees on the stream (capture). The caller
+// holds g_ws_mu until its launches and that record or free are enqueued, so
+// no other call can release the buffer in between.
+hipError_t workspace(size_t bytes, hipStream_t stream, void **p, WsEntry **entry)
+{
+    *entry = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
     hipMemPool_t pool;
-    {
-        std::lock_guard<std::mutex> lk(g_pool_mu);
-        if (!g_pools[dev]) {
-            hipMemPoolProps props;
-            memset(&props, 0, sizeof props);
-            props.allocType = hipMemAllocationTypePinned;
-            props.handleTypes = hipMemHandleTypeNone;
-            props.location.type = hipMemLocationTypeDevice;
-            props.location.id = dev;
-            hipMemPool_t created = nullptr;
-            e = hipMemPoolCreate(&created, &props);
-            if (e != hipSuccess) return e;
-            uint64_t keep = UINT64_MAX;
-            e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
-            if (e != hipSuccess) {
-                (void)hipMemPoolDestroy(created);
-                return e;
-            }
-            g_pools[dev] = created;
-        }
-        pool = g_pools[dev];
+    e = device_pool(dev, &pool);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) return hipMallocFromPoolAsync(p, bytes, pool, stream);
+    WsEntry *hit = nullptr, *lru = &g_ws[0];
+    for (WsEntry &w : g_ws) {
+        if (w.ptr && w.dev == dev && w.stream == stream) hit = &w;
+        if (!w.ptr) lru = &w;
+        else if (lru->ptr && w.last < lru->last) lru = &w;
     }
-    return hipMallocFromPoolAsync(p, bytes, pool, stream);
+    WsEntry *slot = hit ? hit : lru;
+    if (!hit || slot->bytes < bytes) {
+        if (slot->ptr) {
+            e = hipFreeAsync(slot->ptr, slot->stream);   // after the work of its last use
+            slot->ptr = nullptr;
+            if (e != hipSuccess) return e;
+        }
+        if (!slot->done) {
+            e = hipEventCreateWithFlags(&slot->done, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        const size_t want = hit && bytes < 2 * hit->bytes ? 2 * hit->bytes : bytes;   // grow geometrically
+        void *np = nullptr;
+        e = hipMallocFromPoolAsync(&np, want, pool, stream);
+        if (e != hipSuccess) return e;
+        slot->dev = dev;
+        slot->stream = stream;
+        slot->ptr = np;
+        slot->bytes = want;
+    } else {
+        e = hipStreamWaitEvent(stream, slot->done, 0);   // after the buffer's last use
+        if (e != hipSuccess) return e;
+    }
+    slot->last = ++g_ws_clock;
+    *p = slot->ptr;
+    *entry = slot;
+    return hipSuccess;
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;     // bound on M, N, K (index arithmetic)
@@ -115,6 +184,7 @@ int gemm_sizes_ok(int64_t M, int64_t K, int64_t N, int bits)
 {
     const uint64_t lim = (uint64_t)1 << 32;
     if ((uint64_t)M * (uint64_t)K * 2 >= lim) return WQ_ERR_SHAPE;
+    if (N >= ((int64_t)1 << 22)) return WQ_ERR_SHAPE;      // y offsets within a 128-row tile stay below 2^32
     if ((uint64_t)N * (uint64_t)K * (uint64_t)bits / 8 >= lim) return WQ_ERR_SHAPE;
     if ((uint64_t)N * (uint64_t)(K / WQ_BLOCK) * 2 >= lim) return WQ_ERR_SHAPE;
     return gemm_grid_ok(M, N);
@@ -210,10 +280,13 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     if (empty) return WQ_OK;
     st = gemm_sizes_ok(M, K, N, bits);
     if (st) return st;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
     void *ws = nullptr;
-    if (pool_alloc(&ws, (size_t)wq::gemm_ws_bytes(M, K), stream) != hipSuccess) return WQ_ERR_HIP;
+    WsEntry *entry = nullptr;
+    if (workspace((size_t)wq::gemm_ws_bytes(M, K), stream, &ws, &entry) != hipSuccess) return WQ_ERR_HIP;
     const hipError_t e = wq::launch_gemm(x, M, K, N, bits, q, scales, y, ws, stream);
-    const hipError_t f = hipFreeAsync(ws, stream);
+    // the buffer's last use so far (cached), or its release (capture)
+    const hipError_t f = entry ? hipEventRecord(entry->done, stream) : hipFreeAsync(ws, stream);
     return (e == hipSuccess && f == hipSuccess) ? WQ_OK : WQ_ERR_HIP;
 }
 

@@ -85,18 +85,61 @@ __device__ __forceinline__ int row_exponent(float amax)
     return e > 126 ? 126 : e;                // E >= -125 here except for fp32 subnormals
 }
 
-// One row of x -> binary16 in the prepared layout; one wavefront per row.
+// Eight values of group q of a row -> binary16 (times 2^e), in the operand order
+// of the code width, at their place in the prepared row.
+template <int ORDER>
+__device__ __forceinline__ void xprep_store(_Float16 *__restrict__ orow, int q, f4 a, f4 b, int e)
+{
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    h8 hv;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        hv[operand_slot<ORDER == 1 ? 8 : 4>(k)] = (_Float16)ldexpf(v[k], e);   // exact scaling, then nearest even
+    *reinterpret_cast<h8 *>(orow + (q >> 2) * 32 + group_pos(q & 3) * 8) = hv;
+}
+
+__device__ __forceinline__ float absmax8(f4 a, f4 b)
+{
+    return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                 fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+}
+
+// One row of x -> binary16 in the prepared layout; one wavefront per row. Rows
+// of up to 64 * XG groups of 8 values are read once into registers (all loads
+// in flight together); longer rows are read twice.
+constexpr int XG = 8;
 template <int ORDER>
 __device__ __forceinline__ void xprep_row(const float *__restrict__ xrow, int K, _Float16 *__restrict__ orow,
                                           float *__restrict__ rinv_m, int lane)
 {
     const int G = K >> 3;                    // groups of 8 values
     float amax = 0.0f;
+    if (G <= 64 * XG) {
+        f4 va[XG], vb[XG];
+#pragma unroll
+        for (int i = 0; i < XG; ++i) {
+            const int q = lane + 64 * i;
+            if (q < G) {
+                va[i] = *reinterpret_cast<const f4 *>(xrow + 8 * q);
+                vb[i] = *reinterpret_cast<const f4 *>(xrow + 8 * q + 4);
+                amax = fmaxf(amax, absmax8(va[i], vb[i]));
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const int e = row_exponent(amax);
+#pragma unroll
+        for (int i = 0; i < XG; ++i) {
+            const int q = lane + 64 * i;
+            if (q < G) xprep_store<ORDER>(orow, q, va[i], vb[i], e);
+        }
+        if (lane == 0) *rinv_m = ldexpf(1.0f, -e);
+        return;
+    }
     for (int q = lane; q < G; q += 64) {
         const f4 a = *reinterpret_cast<const f4 *>(xrow + 8 * q);
         const f4 b = *reinterpret_cast<const f4 *>(xrow + 8 * q + 4);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+        amax = fmaxf(amax, absmax8(a, b));
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
@@ -104,13 +147,7 @@ __device__ __forceinline__ void xprep_row(const float *__restrict__ xrow, int K,
     for (int q = lane; q < G; q += 64) {
         const f4 a = *reinterpret_cast<const f4 *>(xrow + 8 * q);
         const f4 b = *reinterpret_cast<const f4 *>(xrow + 8 * q + 4);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        h8 h;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            h[operand_slot<ORDER == 1 ? 8 : 4>(k)] = (_Float16)ldexpf(v[k], e);   // exact scaling, then nearest even
-        const int blk = q >> 2;
-        *reinterpret_cast<h8 *>(orow + blk * 32 + group_pos(q & 3) * 8) = h;
+        xprep_store<ORDER>(orow, q, a, b, e);
     }
     if (lane == 0) *rinv_m = ldexpf(1.0f, -e);
 }
@@ -150,20 +187,22 @@ __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__res
 // ---------------------------------------------------------------- GEMM tile
 
 // LDS of one stage of one K slice: the prepared x (BM rows x 128 bytes), then for
-// each of the WN wavefronts its codes (B), int5 bit-4 dwords (H) and scales (S:
-// for each (block, column) the aligned dword holding that block's scale).
+// each of the WN wavefronts its codes (B), int5 bit-4 dwords (H), scales (S: for
+// each (block, column) the aligned dword holding that block's scale) and row
+// factors (R: 2^-e of BM / WN tile rows, repeated over 64 dwords).
 template <int BITS, int BM, int WN>
 struct Lay {
     static constexpr int A = BM * 128;
     static constexpr int BW = 32 * KT * (BITS == 8 ? 32 : 16);   // codes of 32 columns
     static constexpr int HW = BITS == 5 ? 32 * KT * 4 : 0;
     static constexpr int SW = 32 * KT * 4;
-    static constexpr int WAVE = BW + HW + SW;
+    static constexpr int RW = 64 * 4;
+    static constexpr int WAVE = BW + HW + SW + RW;
     static constexpr int STAGE = A + WN * WAVE;
 };
 template <int BM, int WN>
 constexpr int stage_max() { return Lay<8, BM, WN>::STAGE; }   // int8 has the largest stage
-static_assert(Lay<8, 128, 4>::STAGE >= Lay<5, 128, 4>::STAGE && Lay<8, 32, 4>::STAGE >= Lay<5, 32, 4>::STAGE, "");
+static_assert(Lay<8, 128, 4>::STAGE >= Lay<5, 128, 4>::STAGE && Lay<8, 64, 4>::STAGE >= Lay<5, 64, 4>::STAGE, "");
 
 // Buffer loads in the LDS-direct form: lane i writes its 16 (4) bytes at LDS
 // byte address lds + 16 i (4 i); lds (in M0) and the resource are uniform. They
@@ -208,39 +247,56 @@ __device__ __forceinline__ void wait_vm()
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+constexpr int cap63(int n) { return n < 63 ? n : 63; }
 
-// Launch bounds: workgroups of WN * SK wavefronts; 2 resident per compute unit
-// for 4-wavefront groups.
-#define WQ_GEMM_BOUNDS(WN, SK) __launch_bounds__((WN) * (SK) * 64, ((WN) * (SK) <= 4 ? 2 : 1))
+// Bytes of one K slice of a ring buffer: the stage, and with a K split at least
+// the 16 KiB through which a slice hands one fragment of sums to slice 0.
+template <int STAGE, int WN, int SK>
+constexpr int slice_bytes() { return (SK > 1 && STAGE < WN * 4096) ? WN * 4096 : STAGE; }
 
-template <int BITS, int BM, int WN, int SK, int NS>
+// SL: bytes of one K slice of a ring buffer (from the code width's own stage for
+// a single call, from the largest over code widths for a grouped launch).
+template <int BITS, int BM, int WN, int SK, int NS, int SL = slice_bytes<Lay<BITS, BM, WN>::STAGE, WN, SK>()>
 struct Tile {
     using L = Lay<BITS, BM, WN>;
     static constexpr int RF = BM / 32;                  // row fragments per wavefront
     static constexpr int AI = BM / (8 * WN);            // x copy instructions per wavefront and stage
     static constexpr int BI = BITS == 8 ? 2 : 1;        // code copy instructions
-    static constexpr int V = AI + BI + (BITS == 5 ? 1 : 0) + 1;   // copies per wavefront and stage
-    static constexpr int SLICE = stage_max<BM, WN>();   // bytes of one K slice in a ring buffer
-    static_assert(AI * 8 * WN == BM, "x rows per copy instruction");
+    static constexpr int V = AI + BI + (BITS == 5 ? 1 : 0) + 2;   // copies per wavefront and stage
+    static constexpr int RPW = BM / WN;                 // tile rows whose factors a wavefront copies
+    static constexpr int STORES = RF * 16;              // y stores per wavefront and tile (slice 0)
+    static constexpr int SLICE = SL;
+    static_assert(SL >= L::STAGE, "slice size");
+    static constexpr int LDS = NS * SK * SLICE;
+    static_assert(AI * 8 * WN == BM && RPW >= 8 && 32 % RPW == 0, "tile geometry");
     static_assert(NS >= 2 && NS <= 4, "ring depth");
     static_assert(V * (NS - 2) < 64, "vmcnt");
+    static_assert(SK == 1 || WN * 64 * 16 * 4 <= SLICE, "reduction buffer");
 };
 
-// One BM x (32 WN) output tile (tm, tn) of y = x W^T; every thread of the
-// workgroup calls it. ring0..ring3 are the NS stage buffers (separate LDS
-// objects, so waits on copies into one never hold reads of another), each of
-// SK * SLICE bytes. x16 / rinv: the prepared x of this call.
-template <int BITS, int BM, int WN, int SK, int NS>
-__device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, const float *__restrict__ rinv,
-                                          int M, int K, int N, const uint8_t *__restrict__ q,
-                                          const uint16_t *__restrict__ s, float *__restrict__ y, int tm, int tn,
-                                          uint8_t *ring0, uint8_t *ring1, uint8_t *ring2, uint8_t *ring3)
+// Resident workgroups per compute unit of a configuration (LDS and the
+// launch bounds below).
+template <int LDS, int WN, int SK>
+constexpr int gemm_occupancy() { return WN * SK > 4 ? 1 : (LDS <= 53248 ? 3 : (LDS <= 81920 ? 2 : 1)); }
+
+#define WQ_GEMM_BOUNDS(LDS, WN, SK) __launch_bounds__((WN) * (SK) * 64, (gemm_occupancy<LDS, WN, SK>()))
+
+// The tiles [u = 0, U) of one workgroup, as a stream of K stages: tile_of(u)
+// gives (tm, tn) of the u-th tile. The copies of the next NS - 1 stages are in
+// flight while a stage is computed, across tile boundaries, so a tile's first
+// loads overlap the previous tile's last stages and its stores of y. Every
+// thread of the workgroup calls it, with the same U. ring holds the NS stage
+// buffers of SK * SLICE bytes each.
+template <int BITS, int BM, int WN, int SK, int NS, int SL, class TileOf>
+__device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, const float *__restrict__ rinv,
+                                            int M, int K, int N, const uint8_t *__restrict__ q,
+                                            const uint16_t *__restrict__ s, float *__restrict__ y, int U,
+                                            TileOf tile_of, uint8_t *ring)
 {
-    using T = Tile<BITS, BM, WN, SK, NS>;
+    using T = Tile<BITS, BM, WN, SK, NS, SL>;
     using L = typename T::L;
-    constexpr int RF = T::RF, AI = T::AI, V = T::V, SLICE = T::SLICE;
+    constexpr int RF = T::RF, AI = T::AI, V = T::V, SLICE = T::SLICE, RPW = T::RPW;
     constexpr int BN = 32 * WN;
-    const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int h = wv / WN;                       // K slice
@@ -250,6 +306,7 @@ __device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, cons
     const int NTh = (NT + SK - 1) / SK;          // stages of each slice (past K: scale 0)
     const int st0 = h * NTh;
     const uint32_t qrow = (uint32_t)K * BITS / 8;
+    const int c = lane & 31, g = lane >> 5;     // column of the wavefront; lane half
 
     const sgpr4 xr = raw_rsrc(x16, (uint64_t)M * K * 2);
     const sgpr4 qr = raw_rsrc(q, (uint64_t)N * qrow);
@@ -258,35 +315,42 @@ __device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, cons
     // in the same 16-byte granule as the scale (the array is 16-byte aligned),
     // hence in a mapped page, and are never used.
     const sgpr4 sr = raw_rsrc(s, ((uint64_t)N * C * 2 + 3) & ~(uint64_t)3);
+    // Row factors: the region is padded to 256 bytes; tile rows past it read 0
+    // (they are never stored).
+    const sgpr4 rr = raw_rsrc(rinv, gemm_ws_rinv_bytes(M));
 
-    // ---- per-lane copy offsets (the stage enters through the scalar offset)
-    uint32_t xoff[AI];
+    // ---- issue cursor: the next stage to copy and the per-lane offsets of its tile
+    int iu = 0, istl = 0;
+    uint32_t xoff[AI], qoff = 0, hoff = 0, soff = 0, roff = 0;
+    auto set_tile = [&](int u) {
+        const auto tt = tile_of(u);
+        const int m0 = tt.x * BM, n0 = tt.y * BN;
 #pragma unroll
-    for (int j = 0; j < AI; ++j) {
-        const int r = (w * AI + j) * 8 + (lane >> 3);          // tile row written by this lane
-        const int sl = (lane & 7) ^ ((r >> 1) & 7);            // the logical slot stored at slot lane & 7
-        int m = m0 + r;
-        m = m < M ? m : M - 1;
-        xoff[j] = (uint32_t)m * (uint32_t)K * 2 + (uint32_t)(sl >> 2) * 64 + (uint32_t)(sl & 3) * 16;
-    }
-    const int c = lane & 31, g = lane >> 5;     // column of the tile slice; lane half
-    int ncl = n0 + w * 32 + c;
-    ncl = ncl < N ? ncl : N - 1;
-    // codes: lane (c, g) copies block g of the stage for column c (int8: each of
-    // the two copy instructions moves one 16-byte half of it)
-    const uint32_t qoff = (uint32_t)ncl * qrow + (uint32_t)g * (BITS == 8 ? 32 : 16);
-    const uint32_t hoff = (uint32_t)ncl * qrow + (uint32_t)K / 2 + (uint32_t)g * 4;
-    // scales: lane (c, g) copies the aligned dword holding the scale of block
-    // 2 st + g of column c
-    const uint32_t sidx = (uint32_t)ncl * (uint32_t)C + (uint32_t)g;
-    const uint32_t soff = (sidx * 2) & ~3u;
-
-    // Loads of stage stl into ring buffer `slot`. Issued unconditionally (the
-    // compiler's wait counting then sees the same loads on every path); a stage
-    // past the slice's last re-reads the last one (cache hits), into a buffer
-    // that is never read again.
-    auto issue = [&](int stl, uint8_t *ring) {
-        const int st = st0 + (stl < NTh ? stl : NTh - 1);
+        for (int j = 0; j < AI; ++j) {
+            const int r = (w * AI + j) * 8 + (lane >> 3);      // tile row written by this lane
+            const int sl = (lane & 7) ^ ((r >> 1) & 7);        // the logical slot stored at slot lane & 7
+            int m = m0 + r;
+            m = m < M ? m : M - 1;
+            xoff[j] = (uint32_t)m * (uint32_t)K * 2 + (uint32_t)(sl >> 2) * 64 + (uint32_t)(sl & 3) * 16;
+        }
+        int ncl = n0 + w * 32 + c;
+        ncl = ncl < N ? ncl : N - 1;
+        // codes: lane (c, g) copies block g of the stage for column c (int8: each
+        // of the two copy instructions moves one 16-byte half of it)
+        qoff = (uint32_t)ncl * qrow + (uint32_t)g * (BITS == 8 ? 32 : 16);
+        hoff = (uint32_t)ncl * qrow + (uint32_t)K / 2 + (uint32_t)g * 4;
+        // scales: the aligned dword holding the scale of block 2 st + g of column c
+        soff = (((uint32_t)ncl * (uint32_t)C + (uint32_t)g) * 2) & ~3u;
+        roff = (uint32_t)(m0 + w * RPW + lane % RPW) * 4;
+    };
+    set_tile(0);
+    // Copies of the next stage into `ring`. Issued unconditionally (every
+    // wavefront issues V copies per call, which the waits count); past the
+    // last stage the last one is read again (cache hits) into a buffer that is
+    // never read.
+    auto issue = [&](uint8_t *ring) {
+        const bool live = iu < U;
+        const int st = st0 + (live ? istl : NTh - 1);
         uint8_t *base = ring + h * SLICE;
         uint8_t *wb = base + L::A + w * L::WAVE;
 #pragma unroll
@@ -299,6 +363,11 @@ __device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, cons
             if constexpr (BITS == 5) dma4(qr, lds_addr(wb + L::BW), hoff, (uint32_t)st * 8);
         }
         dma4(sr, lds_addr(wb + L::BW + L::HW), soff, (uint32_t)st * 4);
+        dma4(rr, lds_addr(wb + L::BW + L::HW + L::SW), roff, 0);
+        if (live && ++istl == NTh) {
+            istl = 0;
+            if (++iu < U) set_tile(iu);
+        }
     };
 
     // ---- per-lane read offsets
@@ -307,9 +376,6 @@ __device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, cons
 #pragma unroll
     for (int u = 0; u < 2 * KT; ++u) aoff[u] = (uint32_t)c * 128 + (uint32_t)(((2 * u) ^ t) << 4);
     const uint32_t boff = BITS == 8 ? (uint32_t)(g * 1024 + c * 16) : (uint32_t)(c * 16 + g * 8);
-    // which half of the copied dword holds the scale of block kb of column c
-    const uint32_t scol = (uint32_t)ncl * (uint32_t)C;
-    const int ssh[KT] = {(int)((scol & 1) * 16), (int)(((scol + 1) & 1) * 16)};
     const DecodeConsts dc = DecodeConsts::make();
     Decode5Consts dc5;
     if constexpr (BITS == 5) dc5 = Decode5Consts::make();
@@ -321,8 +387,21 @@ __device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, cons
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
     const f16v zero = {};
 
-    auto compute = [&](int stl, const uint8_t *ring) {
-        const int st = st0 + stl;
+    // ---- compute cursor
+    int cu = 0, cstl = 0;
+    int ssh[KT];                                 // which half of a copied dword holds block kb's scale
+    auto set_scale_halves = [&](int u) {
+        const auto tt = tile_of(u);
+        int ncl = tt.y * BN + w * 32 + c;
+        ncl = ncl < N ? ncl : N - 1;
+        const uint32_t scol = (uint32_t)ncl * (uint32_t)C;
+#pragma unroll
+        for (int kb = 0; kb < KT; ++kb) ssh[kb] = (int)(((scol + kb) & 1) * 16);
+    };
+    set_scale_halves(0);
+
+    auto compute = [&](const uint8_t *ring) {
+        const int st = st0 + cstl;
         const uint8_t *A = ring + h * SLICE;
         const uint8_t *wb = A + L::A + w * L::WAVE;
 #pragma unroll
@@ -366,132 +445,145 @@ __device__ __forceinline__ void gemm_tile(const _Float16 *__restrict__ x16, cons
         }
     };
 
-    // Stage stl (in ring buffer `slot`): wait for this wavefront's loads of it
-    // (exactly NS - 2 later stages are in flight behind it), barrier (everyone's
-    // copies have landed and everyone is done with the buffer about to be
-    // refilled), refill that buffer (`nxt`) with stage stl + NS - 1, compute.
-    auto step = [&](int stl, const uint8_t *cur, uint8_t *nxt) {
-        wait_vm<V * (NS - 2)>();
-        lds_barrier();
-        issue(stl + NS - 1, nxt);
-        compute(stl, cur);
-    };
-
-    issue(0, ring0);
-    if constexpr (NS >= 3) issue(1, ring1);
-    if constexpr (NS >= 4) issue(2, ring2);
-    int sb = 0;
-    for (; sb + NS <= NTh; sb += NS) {
-        if constexpr (NS == 2) {
-            step(sb, ring0, ring1);
-            step(sb + 1, ring1, ring0);
-        } else if constexpr (NS == 3) {
-            step(sb, ring0, ring2);
-            step(sb + 1, ring1, ring0);
-            step(sb + 2, ring2, ring1);
-        } else {
-            step(sb, ring0, ring3);
-            step(sb + 1, ring1, ring0);
-            step(sb + 2, ring2, ring1);
-            step(sb + 3, ring3, ring2);
-        }
-    }
-    if (sb < NTh) step(sb, ring0, NS == 2 ? ring1 : (NS == 3 ? ring2 : ring3));
-    if (NS >= 3 && sb + 1 < NTh) step(sb + 1, ring1, ring0);
-    if (NS >= 4 && sb + 2 < NTh) step(sb + 2, ring2, ring1);
-    // the copies of the stages past the end are still in flight: let them land
-    // before the LDS is reused or released
-    wait_vm<0>();
-    lds_barrier();
-
-    if constexpr (SK > 1) {
-        // slices 1..SK-1 hand their partial sums to slice 0 through LDS, one
-        // fragment at a time, in slice order (a fixed order: deterministic)
-        float *red = reinterpret_cast<float *>(ring0);
-        static_assert(WN * 64 * 16 * 4 <= SK * T::SLICE, "reduction buffer");
+    // The end of tile u, whose last stage was computed from `ring`: slices
+    // 1..SK-1 hand their sums to slice 0 through their own parts of that buffer
+    // (free until the next barrier), one fragment at a time in slice order (a
+    // fixed order: deterministic); slice 0 scales by 2^-e_m and stores y with
+    // buffer stores (out-of-range outputs go past the resource and are dropped,
+    // so every wavefront of slice 0 issues exactly STORES stores).
+    auto epilogue = [&](int u, const uint8_t *ring) {
+        if constexpr (SK > 1) {
 #pragma unroll
-        for (int j = 1; j < SK; ++j) {
+            for (int j = 1; j < SK; ++j) {
+#pragma unroll
+                for (int i = 0; i < RF; ++i) {
+                    float *red = reinterpret_cast<float *>(const_cast<uint8_t *>(ring) + j * SLICE);
+                    lds_barrier();
+                    if (h == j) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) red[(v * WN + w) * 64 + lane] = acc[i][v];
+                    }
+                    lds_barrier();
+                    if (h == 0) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[i][v] += red[(v * WN + w) * 64 + lane];
+                    }
+                }
+            }
+        }
+        if (h == 0) {
+            const auto tt = tile_of(u);
+            const int m0 = tt.x * BM, n0 = tt.y * BN;
+            const int rows = M - m0 < BM ? M - m0 : BM;
+            const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + (size_t)m0 * N, (uint64_t)rows * N * 4);
+            const int n = n0 + w * 32 + c;
+            // Output (r, n) of the tile is at byte (r N + n) 4 of yr: a per-lane part
+            // (4 g rows and the column; past N: the resource size, so that every
+            // store of that column lands past the resource and is dropped) and a
+            // uniform part (the rest of the row) in the scalar offset.
+            const uint32_t lane_off = n < N ? (uint32_t)(4 * g * N + n) * 4 : (uint32_t)rows * N * 4;
+            const uint8_t *R = ring + L::A + L::BW + L::HW + L::SW + 16 * g;   // slice 0's factors
+            // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4, column l%32
 #pragma unroll
             for (int i = 0; i < RF; ++i) {
-                lds_barrier();
-                if (h == j) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) red[(v * WN + w) * 64 + lane] = acc[i][v];
-                }
-                lds_barrier();
-                if (h == 0) {
+                for (int j = 0; j < 4; ++j) {
+                    const int rg = i * 32 + 8 * j;                    // rows rg + 4 g .. rg + 4 g + 3
+                    const f4 f = *reinterpret_cast<const f4 *>(R + (rg / RPW) * L::WAVE + (rg % RPW) * 4);
+                    const float fv[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][v] += red[(v * WN + w) * 64 + lane];
+                    for (int v = 0; v < 4; ++v)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[i][4 * j + v] * fv[v]),
+                                                              yr, lane_off, (uint32_t)(rg + v) * N * 4, kNonTemporal);
                 }
             }
         }
-        if (h > 0) return;
-    }
+#pragma unroll
+        for (int i = 0; i < RF; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+    };
 
-    // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
-    // column l%32; y = acc * 2^-e_m.
-    // the factors' region is padded to 256 bytes, so the 4-row loads of rows < M
-    // stay inside it (rows >= M are loaded but never stored)
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rinv, gemm_ws_rinv_bytes(M));
-    const int n = n0 + w * 32 + c;
-    const bool whole = m0 + BM <= M && n0 + BN <= N;
-#pragma unroll
-    for (int i = 0; i < RF; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int mr = m0 + i * 32 + 8 * j + 4 * g;               // rows mr .. mr+3
-            const f4 f = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)mr * 4, 0, 0));
-            const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float val = acc[i][4 * j + u] * fv[u];
-                if (whole) {
-                    __builtin_nontemporal_store(val, y + (size_t)(mr + u) * N + n);
-                } else if (mr + u < M && n < N) {
-                    __builtin_nontemporal_store(val, y + (size_t)(mr + u) * N + n);
-                }
-            }
+    // Stage steps. Each waits for this wavefront's copies of the stage it
+    // computes: NS - 2 later stages are in flight behind them, plus the stores
+    // of tiles ended since those copies were issued, then a barrier (everyone's
+    // copies have landed and everyone is done with the buffer about to be
+    // refilled), refills that buffer with the stage NS - 1 ahead, computes.
+    const int J = U * NTh;
+    constexpr int SKS = SK * SLICE;
+    issue(ring);
+    if constexpr (NS >= 3) issue(ring + SKS);
+    if constexpr (NS >= 4) issue(ring + 2 * SKS);
+    int epi = 0;                                 // bit i: the step i + 1 steps back ended a tile
+    int cs = 0;                                  // ring buffer of the stage computed next
+    for (int j = 0; j < J; ++j) {
+        if (h == 0 && (epi & ((1 << (NS - 1)) - 1)) != 0) {
+            // stores were issued after this stage's copies: count at least one tile's
+            // worth of them (capped: a smaller count only waits longer)
+            wait_vm<cap63(V * (NS - 2) + T::STORES)>();
+        } else {
+            wait_vm<V * (NS - 2)>();
         }
+        lds_barrier();
+        const int ns = cs == 0 ? NS - 1 : cs - 1;   // the buffer computed last step: refill it
+        issue(ring + ns * SKS);
+        const uint8_t *cur = ring + cs * SKS;
+        compute(cur);
+        epi <<= 1;
+        if (++cstl == NTh) {
+            epilogue(cu, cur);
+            epi |= 1;
+            cstl = 0;
+            if (++cu < U) set_scale_halves(cu);
+        }
+        cs = cs + 1 == NS ? 0 : cs + 1;
     }
+    // the copies of the stages past the end are still in flight: let them land
+    // before the LDS is released
+    wait_vm<0>();
 }
 
+// Single call: a persistent grid of G workgroups (a multiple of 8). Workgroup b
+// runs on XCD b % 8; XCD x owns the consecutive tiles [x per, (x + 1) per) of
+// the row-major tile order (neighbouring tiles share rows of x in that XCD's
+// L2), and its workgroups take them round-robin.
 template <int BITS, int BM, int WN, int SK, int NS>
-__global__ WQ_GEMM_BOUNDS(WN, SK) void gemm_kernel(const _Float16 *__restrict__ x16, const float *__restrict__ rinv,
-                                                    int M, int K, int N, const uint8_t *__restrict__ q,
-                                                    const uint16_t *__restrict__ s, float *__restrict__ y,
-                                                    int tiles_m, int tiles_n)
+__global__ WQ_GEMM_BOUNDS((Tile<BITS, BM, WN, SK, NS>::LDS), WN, SK) void gemm_kernel(const _Float16 *__restrict__ x16,
+                                                           const float *__restrict__ rinv, int M, int K, int N,
+                                                           const uint8_t *__restrict__ q,
+                                                           const uint16_t *__restrict__ s, float *__restrict__ y,
+                                                           int tiles_m, int tiles_n)
 {
-    constexpr int SZ = SK * Tile<BITS, BM, WN, SK, NS>::SLICE;
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[SZ];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[SZ];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS >= 3 ? SZ : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS >= 4 ? SZ : 16];
-    // XCD-aware tile order: workgroups id, id+8, id+16, ... run on one XCD; give
-    // them consecutive tiles (row-major over (tm, tn)).
+    __shared__ __attribute__((aligned(16))) uint8_t ring[Tile<BITS, BM, WN, SK, NS>::LDS];
     const int T = tiles_m * tiles_n;
     const int per = (T + kXcds - 1) / kXcds;
-    const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    if (tile >= T) return;
-    const int tm = tile / tiles_n;
-    gemm_tile<BITS, BM, WN, SK, NS>(x16, rinv, M, K, N, q, s, y, tm, tile - tm * tiles_n, ring0, ring1, ring2,
-                                    ring3);
+    const int g8 = (int)gridDim.x / kXcds;
+    const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
+    const int first = x * per + i;
+    const int end = (x + 1) * per < T ? (x + 1) * per : T;
+    const int U = first < end ? (end - first + g8 - 1) / g8 : 0;
+    if (U == 0) return;
+    auto tile_of = [&](int u) {
+        const int tt = first + u * g8;
+        const int tm = tt / tiles_n;
+        return make_int2(tm, tt - tm * tiles_n);
+    };
+    gemm_stream<BITS, BM, WN, SK, NS, Tile<BITS, BM, WN, SK, NS>::SLICE>(x16, rinv, M, K, N, q, s, y, U, tile_of, ring);
 }
 
 // Grouped prefill: the work items of every tensor of a planned table in one
-// launch. Item i belongs to the entry whose [tile_begin, tile_begin + tiles)
-// holds it; within an entry, item j is tile (j % tiles_m, j / tiles_m), so with
-// entries starting at multiples of 8 the items of one XCD (i % 8) share row
-// tiles of x. Items past an entry's tiles (alignment padding) do nothing.
+// launch, one tile per workgroup. Item i belongs to the entry whose
+// [tile_begin, tile_begin + tiles) holds it; within an entry, item j is tile
+// (j % tiles_m, j / tiles_m), so with entries starting at multiples of 8 the
+// items of one XCD (i % 8) share row tiles of x. Items past an entry's tiles
+// (alignment padding) do nothing.
 template <int BM, int WN, int SK, int NS>
-__global__ WQ_GEMM_BOUNDS(WN, SK) void gemm_grouped_kernel(const uint8_t *__restrict__ base,
-                                                           const wq_desc *__restrict__ table, int count, int M,
-                                                           const uint8_t *__restrict__ ws)
+__global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>(), WN, SK>()>::LDS), WN, SK) void gemm_grouped_kernel(const uint8_t *__restrict__ base,
+                                                                   const wq_desc *__restrict__ table, int count,
+                                                                   int M, const uint8_t *__restrict__ ws)
 {
-    constexpr int SZ = SK * Tile<8, BM, WN, SK, NS>::SLICE;
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[SZ];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[SZ];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS >= 3 ? SZ : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS >= 4 ? SZ : 16];
+    constexpr int SL = slice_bytes<stage_max<BM, WN>(), WN, SK>();
+    __shared__ __attribute__((aligned(16))) uint8_t ring[Tile<8, BM, WN, SK, NS, SL>::LDS];
     const int64_t item = blockIdx.x;
     const int tiles_m = (M + BM - 1) / BM;
     int e = -1;
@@ -503,7 +595,8 @@ __global__ WQ_GEMM_BOUNDS(WN, SK) void gemm_grouped_kernel(const uint8_t *__rest
     if (e < 0) return;
     const wq_desc &d = table[e];
     const int j = (int)(item - d.tile_begin);
-    const int tm = j % tiles_m, tn = j / tiles_m;
+    const int2 tile = make_int2(j % tiles_m, j / tiles_m);
+    auto tile_of = [&](int) { return tile; };
     const int K = (int)d.K, N = (int)d.N;
     const uint8_t *q = base + d.q_off;
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(base + d.s_off);
@@ -511,11 +604,25 @@ __global__ WQ_GEMM_BOUNDS(WN, SK) void gemm_grouped_kernel(const uint8_t *__rest
     const _Float16 *x16 = reinterpret_cast<const _Float16 *>(slot);
     const float *rinv = reinterpret_cast<const float *>(slot + gemm_ws_x16_bytes(M, K));
     if (d.bits == 4)
-        gemm_tile<4, BM, WN, SK, NS>(x16, rinv, M, K, N, q, sc, d.y, tm, tn, ring0, ring1, ring2, ring3);
+        gemm_stream<4, BM, WN, SK, NS, SL>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring);
     else if (d.bits == 5)
-        gemm_tile<5, BM, WN, SK, NS>(x16, rinv, M, K, N, q, sc, d.y, tm, tn, ring0, ring1, ring2, ring3);
+        gemm_stream<5, BM, WN, SK, NS, SL>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring);
     else
-        gemm_tile<8, BM, WN, SK, NS>(x16, rinv, M, K, N, q, sc, d.y, tm, tn, ring0, ring1, ring2, ring3);
+        gemm_stream<8, BM, WN, SK, NS, SL>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring);
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus()
+{
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
 template <int BITS, int BM, int WN, int SK, int NS>
@@ -524,31 +631,44 @@ hipError_t launch_cfg(const _Float16 *x16, const float *rinv, int64_t M, int64_t
 {
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + 32 * WN - 1) / (32 * WN));
-    const int T = tiles_m * tiles_n;
-    const unsigned grid = (unsigned)(((T + kXcds - 1) / kXcds) * kXcds);
+    const int64_t T = (int64_t)tiles_m * tiles_n;
+    // persistent grid: every resident workgroup slot, a multiple of 8 (one per XCD)
+    const int64_t slots =
+        (int64_t)device_cus() * gemm_occupancy<Tile<BITS, BM, WN, SK, NS>::LDS, WN, SK>() / kXcds * kXcds;
+    const int64_t want = (T + kXcds - 1) / kXcds * kXcds;
+    const unsigned grid = (unsigned)(want < slots ? want : slots);
     gemm_kernel<BITS, BM, WN, SK, NS><<<grid, WN * SK * 64, 0, stream>>>(
         x16, rinv, (int)M, (int)K, (int)N, (const uint8_t *)q, scales, y, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-// Tile shape, K split and ring depth of a single call:
-//  - long prefills (at least 512 tiles of 128 x 128): 128-row tiles, each code
-//    unpack feeding four row fragments, three stages in flight, two
-//    workgroups per compute unit;
-//  - 256..511 such tiles: the same tiles with the K loop split over two
+// Tile shape, K split and ring depth of a single call (C compute units):
+//  - long prefills (at least 2 C tiles of 128 x 128): 128-row tiles, each code
+//    unpack feeding four row fragments; three workgroups per compute unit with
+//    two stages in flight when that gives no more tiles per compute unit than
+//    two workgroups with three stages (the M = 4096 gate projection: 768 tiles,
+//    one per workgroup, measured 11% faster), else the latter;
+//  - C .. 2 C such tiles: the same tiles with the K loop of each split over two
 //    wavefront groups of one workgroup;
 //  - fewer: 64-row tiles (the M = 64 int8 lm_head has 1187 of them) with four
 //    stages in flight, or for few of those, 64-row tiles with a two-way split.
+// The grid is persistent (every resident workgroup slot), so the tiles of a
+// workgroup stream through one copy ring.
 template <int BITS>
 hipError_t launch_shape(const _Float16 *x16, const float *rinv, int64_t M, int64_t K, int64_t N, const void *q,
                         const uint16_t *scales, float *y, hipStream_t stream)
 {
+    const int64_t cus = device_cus();
     const int64_t tn = (N + 127) / 128;
     const int64_t t128 = ((M + 127) / 128) * tn;
     const int64_t t64 = ((M + 63) / 64) * tn;
-    if (M > 64 && t128 >= 512) return launch_cfg<BITS, 128, 4, 1, 3>(x16, rinv, M, K, N, q, scales, y, stream);
-    if (M > 64 && t128 >= 256) return launch_cfg<BITS, 128, 4, 2, 3>(x16, rinv, M, K, N, q, scales, y, stream);
-    if (t64 >= 256) return launch_cfg<BITS, 64, 4, 1, 4>(x16, rinv, M, K, N, q, scales, y, stream);
+    if (M > 64 && t128 >= 2 * cus) {
+        const int64_t per3 = 3 * ((t128 + 3 * cus - 1) / (3 * cus)), per2 = 2 * ((t128 + 2 * cus - 1) / (2 * cus));
+        if (per3 <= per2) return launch_cfg<BITS, 128, 4, 1, 2>(x16, rinv, M, K, N, q, scales, y, stream);
+        return launch_cfg<BITS, 128, 4, 1, 3>(x16, rinv, M, K, N, q, scales, y, stream);
+    }
+    if (M > 64 && t128 >= cus) return launch_cfg<BITS, 128, 4, 2, 3>(x16, rinv, M, K, N, q, scales, y, stream);
+    if (t64 >= cus) return launch_cfg<BITS, 64, 4, 1, 4>(x16, rinv, M, K, N, q, scales, y, stream);
     return launch_cfg<BITS, 64, 4, 2, 3>(x16, rinv, M, K, N, q, scales, y, stream);
 }
 

@@ -109,11 +109,20 @@ def _torch():
     return torch
 
 
-def _stream(stream=None) -> int:
+_raw_stream = None
+
+
+def _stream(stream=None, device=None) -> int:
+    """Raw hipStream_t of `stream`, else of the current stream of `device`."""
+    global _raw_stream
+    if stream is not None:
+        return int(stream.cuda_stream)
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream)
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream and device is not None:
+        return int(_raw_stream(device))
+    return int(torch.cuda.current_stream().cuda_stream)
 
 
 def _ptr(t) -> int:
@@ -172,9 +181,9 @@ def unpack(q, K: int, bits: int, stream=None):
 
 def _matmul(fn: str, x, q, scales, bits: int, out=None, stream=None):
     torch = _torch()
-    _dev_tensor(x, torch.float32, "x")
-    _dev_tensor(q, torch.uint8, "q")
-    _dev_tensor(scales, torch.int16, "scales")
+    for t, dt, name in ((x, torch.float32, "x"), (q, torch.uint8, "q"), (scales, torch.int16, "scales")):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dt and t.is_contiguous()):
+            _dev_tensor(t, dt, name)                # raises with the reason
     _need(x.dim() == 2, "x must be [M, K]")
     M, K = x.shape
     N = q.shape[0]
@@ -183,10 +192,13 @@ def _matmul(fn: str, x, q, scales, bits: int, out=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     else:
-        _dev_tensor(out, torch.float32, "out")
+        if not (isinstance(out, torch.Tensor) and out.is_cuda and out.dtype == torch.float32 and out.is_contiguous()):
+            _dev_tensor(out, torch.float32, "out")
         _need(tuple(out.shape) == (M, N), "out must be [M, N]")
-    st = getattr(load(), fn)(_ptr(x), M, K, N, bits, _ptr(q), _ptr(scales), _ptr(out), _stream(stream))
-    _check(st, fn)
+    st = getattr(load(), fn)(x.data_ptr(), M, K, N, bits, q.data_ptr(), scales.data_ptr(), out.data_ptr(),
+                             _stream(stream, x.get_device()))
+    if st:
+        raise WqError(st, fn)
     return out
 
 
