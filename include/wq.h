@@ -62,12 +62,14 @@ enum wq_status {
     WQ_ERR_ALIGN = 4,     /* a pointer or table offset is misaligned */
     WQ_ERR_M_RANGE = 5,   /* M outside the entry point's range (wq_gemv: 1..16) */
     WQ_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
-    WQ_ERR_TABLE = 7      /* a tensor-table entry is inconsistent */
+    WQ_ERR_TABLE = 7,     /* a tensor-table entry is inconsistent */
+    WQ_ERR_SCRATCH = 8    /* wq_gemm_noalloc: the workspace exceeds WQ_NOALLOC_SCRATCH_BYTES */
 };
 
 #define WQ_BLOCK 32           /* values per quantization block along K */
 #define WQ_GEMV_MAX_M 16      /* largest M accepted by wq_gemv */
 #define WQ_TABLE_ALIGN 64     /* alignment of tensors in a package and of table entries */
+#define WQ_NOALLOC_SCRATCH_BYTES (32u << 20)   /* per-device scratch of wq_gemm_noalloc */
 
 /* Bytes of packed codes for an [N][K] tensor: N*K*bits/8. 0 on bad arguments. */
 size_t wq_q_bytes(int64_t N, int64_t K, int bits);
@@ -136,6 +138,22 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
  */
 int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
             const void *q, const uint16_t *scales, float *y, hipStream_t stream);
+
+/*
+ * wq_gemm_noalloc -- wq_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc). Same arguments, kernels, results (bitwise) and error bound as
+ * wq_gemm, but the workspace is a fixed per-device scratch array that lives as
+ * long as the library is loaded: ceil256(2*M*K) + ceil256(4*M) bytes must not
+ * exceed WQ_NOALLOC_SCRATCH_BYTES (32 MiB, e.g. M = 4096 at K = 4096), else
+ * WQ_ERR_SCRATCH and nothing is launched. No allocation is made; the first
+ * call on a device looks up the scratch's address. Every call on a device
+ * shares that device's scratch (nothing in it needs to start at zero), so
+ * calls that overlap on one device, e.g. on two streams, race; calls on one
+ * stream are ordered and safe.
+ */
+int wq_gemm_noalloc(const float *x, int64_t M, int64_t K, int64_t N, int bits,
+                    const void *q, const uint16_t *scales, float *y, hipStream_t stream);
 
 /* wq_linear -- dispatch by M: M <= 16 -> wq_gemv, M > 16 -> wq_gemm. */
 int wq_linear(const float *x, int64_t M, int64_t K, int64_t N, int bits,

@@ -24,10 +24,10 @@ def test_exports_every_header_symbol(lib):
     syms = W.header_symbols()
     assert {"wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_grouped",
             "wq_table_layout", "wq_table_plan", "wq_q_bytes", "wq_s_bytes", "wq_strerror",
-            "wq_embed", "wq_abi_version", "wq_table_plan_gemm", "wq_gemm_grouped"} <= set(syms)
+            "wq_embed", "wq_abi_version", "wq_table_plan_gemm", "wq_gemm_grouped", "wq_gemm_noalloc"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.wq_abi_version() == 5
+    assert lib.wq_abi_version() == 6
 
 
 def test_sizes(lib):
@@ -249,7 +249,22 @@ def test_gemm_grouped_validation(lib):
     assert g(None, None, 0, 0, 64, None, 0, None) == OK
 
 
+def test_gemm_noalloc_scratch_limit(lib):
+    """wq_gemm_noalloc refuses, before anything is launched, a call whose
+    workspace (ceil256(2 M K) + ceil256(4 M) bytes) exceeds its 32 MiB scratch,
+    and validates arguments like wq_gemm."""
+    SCRATCH = 8
+    f = lib.wq_gemm_noalloc
+    assert f(FAKE, 4097, 4096, 64, 4, FAKE, FAKE, FAKE, None) == SCRATCH    # 2 * 4097 * 4096 > 32 MiB
+    assert f(FAKE, 16384, 1024, 64, 4, FAKE, FAKE, FAKE, None) == SCRATCH   # exactly 32 MiB of x + the factors
+    assert f(FAKE, 100, 1024, 64, 6, FAKE, FAKE, FAKE, None) == BITS
+    assert f(None, 100, 1024, 64, 4, FAKE, FAKE, FAKE, None) == NULL
+    assert f(MIS, 100, 1024, 64, 4, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(None, 0, 1024, 64, 4, None, None, None, None) == OK
+    assert lib.wq_strerror(SCRATCH).decode().startswith("workspace larger")
+
+
 def test_strerror(lib):
-    for s in range(8):
+    for s in range(9):
         assert lib.wq_strerror(s).decode()
     assert lib.wq_strerror(99).decode() == "unknown status"

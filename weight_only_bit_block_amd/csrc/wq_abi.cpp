@@ -290,6 +290,21 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     return (e == hipSuccess && f == hipSuccess) ? WQ_OK : WQ_ERR_HIP;
 }
 
+int wq_gemm_noalloc(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
+                    const uint16_t *scales, float *y, hipStream_t stream)
+{
+    bool empty;
+    int st = check_matmul(x, M, K, N, bits, q, scales, y, &empty);
+    if (st) return st;
+    if (empty) return WQ_OK;
+    st = gemm_sizes_ok(M, K, N, bits);
+    if (st) return st;
+    if (wq::gemm_ws_bytes(M, K) > wq::kGemmNoAllocScratch) return WQ_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (wq::gemm_noalloc_scratch(&ws) != hipSuccess) return WQ_ERR_HIP;
+    return hip_status(wq::launch_gemm(x, M, K, N, bits, q, scales, y, ws, stream));
+}
+
 int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits, const void *q,
              const uint16_t *scales, float *out, hipStream_t stream)
 {
@@ -450,10 +465,11 @@ const char *wq_strerror(int status)
     case WQ_ERR_M_RANGE: return "M outside the range of this entry point";
     case WQ_ERR_HIP: return "HIP runtime error at launch";
     case WQ_ERR_TABLE: return "inconsistent tensor-table entry";
+    case WQ_ERR_SCRATCH: return "workspace larger than the scratch of wq_gemm_noalloc";
     default: return "unknown status";
     }
 }
 
-int wq_abi_version(void) { return 5; }
+int wq_abi_version(void) { return 6; }
 
 }  // extern "C"

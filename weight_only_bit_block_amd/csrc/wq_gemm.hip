@@ -52,6 +52,8 @@
 // XCD's L2; y is written with non-temporal stores, scaled by the row's 2^-e_m.
 // The grouped form runs the tiles of every tensor of a planned table in one
 // launch (the projections of a layer), with the same tile body.
+#include <mutex>
+
 #include "wq_internal.h"
 #include "wq_decode.h"
 
@@ -681,7 +683,33 @@ hipError_t launch_grouped(const void *base, const wq_desc *table, int count, int
     return hipGetLastError();
 }
 
+// Scratch of the allocation-free prefill entry point: the prepared x and row
+// factors of one call, in device memory that exists as long as the library is
+// loaded. Host code addresses it only through the pointer hipGetSymbolAddress
+// returns for the current device (the array's name is a host stand-in).
+static __device__ __align__(256) uint8_t scratch[kGemmNoAllocScratch];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
 }  // namespace
+
+hipError_t gemm_noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, void *ws, hipStream_t stream)

@@ -138,6 +138,10 @@ __host__ __device__ inline uint64_t gemm_ws_x16_bytes(int64_t M, int64_t K) { re
 __host__ __device__ inline uint64_t gemm_ws_rinv_bytes(int64_t M) { return gemm_ws_round((uint64_t)M * 4); }
 __host__ __device__ inline uint64_t gemm_ws_bytes(int64_t M, int64_t K) { return gemm_ws_x16_bytes(M, K) + gemm_ws_rinv_bytes(M); }
 
+// Scratch of wq_gemm_noalloc: one per device, for the workspace above.
+constexpr uint64_t kGemmNoAllocScratch = (uint64_t)32 << 20;
+static_assert(kGemmNoAllocScratch == WQ_NOALLOC_SCRATCH_BYTES, "wq.h states the scratch size");
+
 // ---------------------------------------------------------------- grouped prefill geometry
 // A grouped prefill launch uses one tile shape for every tensor, chosen by M
 // alone: BM-row x 128-column tiles, with the K loop of each tile split over S
@@ -167,6 +171,8 @@ hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits
                        const void *q, const uint16_t *scales, float *y, void *ws, hipStream_t stream);
 hipError_t launch_gemm_grouped(const void *base, const wq_desc *table_dev, int count,
                                int64_t total_tiles, int64_t M, void *ws, hipStream_t stream);
+// Device address of this device's scratch of wq_gemm_noalloc (looked up once per device).
+hipError_t gemm_noalloc_scratch(void **ptr);
 hipError_t launch_mgemv(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                         const uint16_t *scales, float *y, hipStream_t stream);
 hipError_t launch_mgemv_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_items,

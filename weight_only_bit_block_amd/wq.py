@@ -65,7 +65,7 @@ def load(path: Optional[str] = None):
     lib.wq_s_bytes.restype = ctypes.c_size_t
     lib.wq_pack.argtypes = [P, I64, I64, I, P, P, P]
     lib.wq_unpack.argtypes = [P, I64, I64, I, P, P]
-    for f in ("wq_gemv", "wq_gemm", "wq_linear"):
+    for f in ("wq_gemv", "wq_gemm", "wq_linear", "wq_gemm_noalloc"):
         getattr(lib, f).argtypes = mm
     lib.wq_table_layout.argtypes = [P, I, ctypes.POINTER(ctypes.c_uint64)]
     lib.wq_table_plan.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64)]
@@ -76,7 +76,7 @@ def load(path: Optional[str] = None):
     lib.wq_strerror.argtypes = [I]
     lib.wq_strerror.restype = ctypes.c_char_p
     lib.wq_abi_version.argtypes = []
-    for f in ("wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_table_layout",
+    for f in ("wq_pack", "wq_unpack", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemm_noalloc", "wq_table_layout",
               "wq_table_plan", "wq_table_plan_gemm", "wq_gemv_grouped", "wq_gemm_grouped", "wq_embed",
               "wq_abi_version"):
         getattr(lib, f).restype = I
@@ -210,6 +210,13 @@ def gemv(x, q, scales, bits: int, out=None, stream=None):
 def gemm(x, q, scales, bits: int, out=None, stream=None):
     """Prefill GEMM (fp16 matrix cores, per-block fp32 scaling), any M."""
     return _matmul("wq_gemm", x, q, scales, bits, out, stream)
+
+
+def gemm_noalloc(x, q, scales, bits: int, out=None, stream=None):
+    """Prefill GEMM on the library's fixed per-device scratch (no device
+    allocation by the library; the workspace must fit WQ_NOALLOC_SCRATCH_BYTES,
+    and calls that overlap on one device race)."""
+    return _matmul("wq_gemm_noalloc", x, q, scales, bits, out, stream)
 
 
 def linear(x, q, scales, bits: int, out=None, stream=None):
