@@ -24,11 +24,11 @@ gate|up) forms of the step, tied-embedding lookups, batched decode of the mixed
 package at M=1, 2, 4, 8 and 16, the int5 step, and the prefill GEMMs (M=4096
 gate/up/down int4 + int8 lm_head on the last 64 rows; one layer's seven
 projections at M=128 and 1024) in TFLOP/s against the fp16 matrix-core peak.
-Prefill numbers are cold: a 1 GiB read+write flush runs before every timed
+Prefill numbers are cold: a 1 GiB read-only flush runs before every timed
 call (median of --prefill-reps); warm numbers are labelled as such. Every
 timed output is NaN-filled first and checked against the oracle on sampled
-rows and columns afterwards. --decode-only runs the decode-step leg alone (the
-profile counter runs use it).
+rows and columns afterwards. --decode-only runs the decode-step leg alone and
+--prefill-only the prefill legs alone (the profile counter runs use them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -96,6 +96,8 @@ def parse():
                     help="only the decode-step leg (the profile counter runs use this)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill legs, printed as one JSON object (the GEMM counter runs use this)")
     ap.add_argument("--prefill-reps", type=int, default=21,
                     help="cold runs per prefill measurement (median reported)")
     return ap.parse_args()
@@ -460,16 +462,19 @@ def int5_leg(torch, wqa, inputs, np, oracle, steps, warmup, flush, reps):
 
 
 class Flush:
-    """Cold-cache protocol: before every cold run a 1 GiB device buffer is read
-    and written (4x the 256 MB last-level cache), on the stream of the run and
-    outside its HIP-event window."""
+    """Cold-cache protocol: before every cold run a 1 GiB device buffer (4x the
+    256 MB last-level cache) is read by a reduction, on the stream of the run
+    and outside its HIP-event window. It writes nothing back: a flush that also
+    wrote the buffer would leave dirty lines whose write-back then competes with
+    the timed call (measured: about 20 us more on the M = 64 lm_head)."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.float32, device="cuda")
 
     def __call__(self):
-        self.buf.add_(1.0)
+        self.torch.sum(self.buf, dim=0, keepdim=True, out=self.sink)
 
 
 def cold_ms(torch, fn, flush, reps):
@@ -571,8 +576,8 @@ def prefill_leg(torch, wqa, inputs, np, oracle, flush, reps):
     tfg = mlp_flops / (g_ms[0] * 1e-3) / 1e12
     return {
         "workload": wl.name,
-        "protocol": f"cold: a 1 GiB read+write flush before every run, median of {reps}; warm: {reps} runs back "
-                    "to back; HIP events around the call only; every call includes its x preparation kernel",
+        "protocol": f"cold: a 1 GiB read-only flush before every run, median of {reps}; warm: {reps} runs back "
+                    "to back; HIP events around the call only; every call includes its x preparation (a pre-pass kernel, or inside the skinny kernel)",
         "calls": {t.name: {"cold_ms": round(per[i][0], 4), "cold_min_ms": round(per[i][1], 4),
                            "cold_max_ms": round(per[i][2], 4), "warm_ms": round(warm[i], 4),
                            "tflops_cold": round(2 * t.M * t.N * t.K / (per[i][0] * 1e-3) / 1e12, 2)}
@@ -641,7 +646,7 @@ def layer_prefill_leg(torch, wqa, inputs, np, oracle, flush, reps):
                         "workgroups": call.total_tiles}
     out["note"] = ("7 int4 projections (q, k, v, o, gate, up, down) of one layer, 1% outlier rows; "
                    "grouped = wq_gemm_grouped (x preparation + one GEMM launch); sequential = 7 wq_gemm calls; "
-                   f"cold = 1 GiB flush before each run, median of {reps}; HIP events")
+                   f"cold = 1 GiB read-only flush before each run, median of {reps}; HIP events")
     return out
 
 
@@ -734,6 +739,17 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.prefill_only:
+        import numpy as np
+        import oracle
+        flush = Flush(torch)
+        log("prefill leg")
+        res = {"prefill": prefill_leg(torch, wqa, inputs, np, oracle, flush, args.prefill_reps)}
+        log("layer prefill leg (grouped prefill launch)")
+        res["layer_prefill"] = layer_prefill_leg(torch, wqa, inputs, np, oracle, flush, args.prefill_reps)
+        print(json.dumps(res), flush=True)
+        return 0
 
     wl = inputs.decode_step(1)
     log(f"packing {len(wl.tensors)} tensors x {COPIES} copies ({wl.weight_bytes} B each)")

@@ -304,6 +304,117 @@ def test_gemm_zero_scales_and_determinism(torch, bits):
         assert np.all(diff <= 1e-5 * abs(f) * B16), name
 
 
+# Few rows and many columns (M <= 64, K in {512, 1024, 2048 at M <= 32}, at
+# least 4 strips of 32 columns per compute unit) run on the skinny kernel: x
+# resident in LDS, prepared in the kernel, weights streamed into registers.
+SKINNY_N = 33000          # 1031 strips of 32 columns and a strip of 8
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,Ms", [(512, (1, 33, 64)), (1024, (17, 40, 64)), (2048, (5, 32))])
+def test_gemm_skinny(torch, bits, K, Ms):
+    """Skinny-kernel shapes against the oracle on sampled columns (the ragged
+    last strip included) and every row: an outlier row, rows that are all zero,
+    and M below the 32- or 64-row tile."""
+    N = SKINNY_N
+    w = _weights(N, K, (60, bits, K))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    rng = inputs.generator((61, bits, K))
+    cols = np.unique(np.concatenate([rng.choice(N, 600, replace=False), np.arange(N - 40, N), [0]]))
+    for M in Ms:
+        x = inputs.normal((M, K), seed=(62, bits, K, M))
+        x[M // 2] *= 20
+        if M > 2:
+            x[1] = 0
+        note(f"gemm skinny bits={bits} M={M} K={K} N={N}")
+        y = to_host(wqa.gemm(to_dev(x), q, s, bits))
+        assert np.all(np.isfinite(y))
+        yc = y[:, cols]
+        y_ref, _ = oracle.matmul(x, q_ref[cols], s_ref[cols], bits)
+        y16, B16 = oracle.matmul(x, q_ref[cols], s_ref[cols], bits, x16=True)
+        check_gemm(yc, y_ref, f"skinny bits={bits} M={M} K={K}")
+        check_gemv(yc, y16, B16, f"skinny vs x16 bits={bits} M={M} K={K}")
+        if M > 2:
+            assert np.all(y[1] == 0)
+        for m in range(M):
+            den = np.linalg.norm(y_ref[m])
+            if den > 0:
+                assert np.linalg.norm(yc[m] - y_ref[m]) <= 2e-3 * den, m
+        # deterministic: the same call gives the same bits
+        y2 = to_host(wqa.gemm(to_dev(x), q, s, bits))
+        assert np.array_equal(y, y2)
+
+
+def _guarded(torch, M, N, pre=4096, post=None):
+    """An [M, N] fp32 output inside a larger buffer whose other elements hold a
+    sentinel; returns (buffer, view, check) where check() asserts that nothing
+    outside the view changed."""
+    post = post if post is not None else 256 * max(N, 1) + 4096
+    buf = torch.full((pre + M * N + post,), 1234.5, dtype=torch.float32, device="cuda")
+    y = buf[pre: pre + M * N].view(M, N)
+
+    def check(what):
+        torch.cuda.synchronize()
+        h = to_host(buf)
+        assert np.all(h[:pre] == 1234.5), f"{what}: write before the output"
+        bad = np.nonzero(h[pre + M * N:] != 1234.5)[0]
+        assert bad.size == 0, f"{what}: {bad.size} writes past the output (first at +{int(bad[0]) if bad.size else 0})"
+        assert np.all(np.isfinite(to_host(y))), f"{what}: an output not written"
+
+    y.fill_(float("nan"))
+    return buf, y, check
+
+
+@pytest.mark.parametrize("case", ["tile64", "tile128_split", "tile128", "skinny", "mgemv", "gemv", "embed"])
+def test_writes_stay_inside_the_output(torch, case):
+    """Every kernel writes its [M, N] output and nothing around it: the output
+    sits inside a buffer of sentinels with 256 rows of room past its end (more
+    than any tile overhangs), at shapes with ragged last row tiles and column
+    strips."""
+    shapes = {"tile64": (130, 96, 300), "tile128_split": (2100, 96, 2000), "tile128": (2100, 96, 4000),
+              "skinny": (40, 512, SKINNY_N), "mgemv": (5, 96, 300), "gemv": (1, 160, 77), "embed": (0, 96, 150)}
+    M, K, N = shapes[case]
+    cid = list(shapes).index(case)
+    bits = 4
+    w = _weights(N, K, (63, cid))
+    q_ref, s_ref = oracle.quantize(w, bits)
+    q, s = to_dev(q_ref), to_dev(s_ref)
+    note(f"guarded output {case} M={M} K={K} N={N}")
+    if case == "embed":
+        ids = np.array([0, N - 1, 7, 3, N - 1], dtype=np.int32)
+        _, y, check = _guarded(torch, len(ids), K)
+        wqa.embed(to_dev(ids), q, s, K, bits, out=y)
+        check(case)
+        return
+    x = to_dev(inputs.normal((M, K), seed=(64, cid)))
+    _, y, check = _guarded(torch, M, N)
+    if case in ("mgemv", "gemv"):
+        wqa.gemv(x, q, s, bits, out=y)
+    else:
+        wqa.gemm(x, q, s, bits, out=y)
+    check(case)
+
+
+def test_grouped_writes_stay_inside_the_outputs(torch):
+    """The grouped prefill (M = 130: 64-row tiles with a ragged tail) and decode
+    (M = 3) launches write every output of their tables and nothing around them."""
+    specs = [(4, 300, 96), (8, 77, 160), (5, 130, 256)]
+    pkg = wqa.Package(specs)
+    for i, (bits, N, K) in enumerate(specs):
+        q_ref, s_ref = oracle.quantize(_weights(N, K, (65, i)), bits)
+        pkg.q(i).copy_(to_dev(q_ref))
+        pkg.scales(i).copy_(to_dev(s_ref))
+    for M, prefill in ((130, True), (3, False)):
+        guards = [_guarded(torch, M, N) for (_, N, _) in specs]
+        xs = [to_dev(inputs.normal((M, K), seed=(66, i, M))) for i, (_, _, K) in enumerate(specs)]
+        call = wqa.GroupedCall(pkg, xs, [g[1] for g in guards], M, prefill=prefill)
+        note(f"guarded grouped M={M} prefill={prefill}")
+        call()
+        for i, g in enumerate(guards):
+            g[2](f"grouped M={M} tensor {i}")
+
+
 def test_linear_dispatch(torch):
     K, N = 1024, 300
     w = _weights(N, K, (16,))

@@ -280,6 +280,8 @@ int wq_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const voi
     if (empty) return WQ_OK;
     st = gemm_sizes_ok(M, K, N, bits);
     if (st) return st;
+    if (wq::gemm_skinny(M, K, N, bits))          // prepares x itself: no workspace
+        return hip_status(wq::launch_gemm(x, M, K, N, bits, q, scales, y, nullptr, stream));
     std::lock_guard<std::mutex> lk(g_ws_mu);
     void *ws = nullptr;
     WsEntry *entry = nullptr;

@@ -53,6 +53,7 @@
 // The grouped form runs the tiles of every tensor of a planned table in one
 // launch (the projections of a layer), with the same tile body.
 #include <mutex>
+#include <type_traits>
 
 #include "wq_internal.h"
 #include "wq_decode.h"
@@ -88,17 +89,21 @@ __device__ __forceinline__ int row_exponent(float amax)
 }
 
 // Eight values of group q of a row -> binary16 (times 2^e), in the operand order
-// of the code width, at their place in the prepared row.
+// of the code width.
 template <int ORDER>
-__device__ __forceinline__ void xprep_store(_Float16 *__restrict__ orow, int q, f4 a, f4 b, int e)
+__device__ __forceinline__ h8 xprep_group(f4 a, f4 b, int e)
 {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     h8 hv;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
         hv[operand_slot<ORDER == 1 ? 8 : 4>(k)] = (_Float16)ldexpf(v[k], e);   // exact scaling, then nearest even
-    *reinterpret_cast<h8 *>(orow + (q >> 2) * 32 + group_pos(q & 3) * 8) = hv;
+    return hv;
 }
+
+// 16-byte slot of group q within a prepared row: block q / 4, position
+// group_pos(q % 4) within the block.
+__device__ __forceinline__ int xprep_slot(int q) { return (q >> 2) * 4 + group_pos(q & 3); }
 
 __device__ __forceinline__ float absmax8(f4 a, f4 b)
 {
@@ -106,13 +111,12 @@ __device__ __forceinline__ float absmax8(f4 a, f4 b)
                  fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
 }
 
-// One row of x -> binary16 in the prepared layout; one wavefront per row. Rows
-// of up to 64 * XG groups of 8 values are read once into registers (all loads
-// in flight together); longer rows are read twice.
-constexpr int XG = 8;
-template <int ORDER>
-__device__ __forceinline__ void xprep_row(const float *__restrict__ xrow, int K, _Float16 *__restrict__ orow,
-                                          float *__restrict__ rinv_m, int lane)
+// One row of x -> binary16 groups in operand order, handed to put(q, h8); one
+// wavefront per row; returns the row's exponent e. Rows of up to 64 * XG
+// groups of 8 values are read once into registers (all loads in flight
+// together); longer rows are read twice.
+template <int ORDER, int XG, class Put>
+__device__ __forceinline__ int xprep_row(const float *__restrict__ xrow, int K, int lane, Put put)
 {
     const int G = K >> 3;                    // groups of 8 values
     float amax = 0.0f;
@@ -133,10 +137,9 @@ __device__ __forceinline__ void xprep_row(const float *__restrict__ xrow, int K,
 #pragma unroll
         for (int i = 0; i < XG; ++i) {
             const int q = lane + 64 * i;
-            if (q < G) xprep_store<ORDER>(orow, q, va[i], vb[i], e);
+            if (q < G) put(q, xprep_group<ORDER>(va[i], vb[i], e));
         }
-        if (lane == 0) *rinv_m = ldexpf(1.0f, -e);
-        return;
+        return e;
     }
     for (int q = lane; q < G; q += 64) {
         const f4 a = *reinterpret_cast<const f4 *>(xrow + 8 * q);
@@ -149,8 +152,18 @@ __device__ __forceinline__ void xprep_row(const float *__restrict__ xrow, int K,
     for (int q = lane; q < G; q += 64) {
         const f4 a = *reinterpret_cast<const f4 *>(xrow + 8 * q);
         const f4 b = *reinterpret_cast<const f4 *>(xrow + 8 * q + 4);
-        xprep_store<ORDER>(orow, q, a, b, e);
+        put(q, xprep_group<ORDER>(a, b, e));
     }
+    return e;
+}
+
+// One row of x into the prepared workspace layout (global memory).
+template <int ORDER>
+__device__ __forceinline__ void xprep_row_ws(const float *__restrict__ xrow, int K, _Float16 *__restrict__ orow,
+                                             float *__restrict__ rinv_m, int lane)
+{
+    const int e = xprep_row<ORDER, 8>(xrow, K, lane,
+                                   [&](int q, h8 hv) { *reinterpret_cast<h8 *>(orow + xprep_slot(q) * 8) = hv; });
     if (lane == 0) *rinv_m = ldexpf(1.0f, -e);
 }
 
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(256) void xprep_kernel(const float *__restrict__ x,
 {
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
-    xprep_row<ORDER>(x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
+    xprep_row_ws<ORDER>(x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
 }
 
 // Grouped: entry e (blockIdx.y) prepares its x unless it is empty or an earlier
@@ -182,8 +195,8 @@ __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__res
     uint8_t *base = ws + (size_t)slot * kGemmWsUnit;
     _Float16 *x16 = reinterpret_cast<_Float16 *>(base);
     float *rinv = reinterpret_cast<float *>(base + gemm_ws_x16_bytes(M, K));
-    if (d.bits == 8) xprep_row<1>(d.x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
-    else xprep_row<0>(d.x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
+    if (d.bits == 8) xprep_row_ws<1>(d.x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
+    else xprep_row_ws<0>(d.x + (size_t)m * K, K, x16 + (size_t)m * K, rinv + m, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------- GEMM tile
@@ -480,9 +493,10 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
             const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + (size_t)m0 * N, (uint64_t)rows * N * 4);
             const int n = n0 + w * 32 + c;
             // Output (r, n) of the tile is at byte (r N + n) 4 of yr: a per-lane part
-            // (4 g rows and the column; past N: the resource size, so that every
-            // store of that column lands past the resource and is dropped) and a
-            // uniform part (the rest of the row) in the scalar offset.
+            // (4 g rows and the column; past N: the resource size) plus the rest of
+            // the row, both in the vector offset, which alone is range-checked:
+            // rows past the tile's last and columns past N land past the resource
+            // and are dropped. (r + rows) N 4 < 2^32 as N < 2^22.
             const uint32_t lane_off = n < N ? (uint32_t)(4 * g * N + n) * 4 : (uint32_t)rows * N * 4;
             const uint8_t *R = ring + L::A + L::BW + L::HW + L::SW + 16 * g;   // slice 0's factors
             // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4, column l%32
@@ -496,7 +510,7 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[i][4 * j + v] * fv[v]),
-                                                              yr, lane_off, (uint32_t)(rg + v) * N * 4, kNonTemporal);
+                                                              yr, lane_off + (uint32_t)(rg + v) * N * 4, 0, kNonTemporal);
                 }
             }
         }
@@ -627,6 +641,235 @@ int device_cus()
     return cus[dev];
 }
 
+// ---------------------------------------------------------------- skinny GEMM
+// With few rows (M <= 64) and many columns (the lm_head at M = 64) the GEMM is
+// bound by streaming the weights from HBM, and the tile kernel above, which
+// passes every operand through one LDS ring per workgroup, keeps too few bytes
+// in flight per compute unit for that. Here one workgroup per compute unit
+// first rounds all M rows of x to binary16 into LDS (the per-row power-of-two
+// scaling and operand order of xprep_kernel, so no pre-pass and no workspace),
+// where they stay for the whole launch; then each of its 8 wavefronts walks
+// 32-column strips of the weights, loading the codes and scales of SB blocks
+// at a time straight into registers with the next SKP - 1 batches in flight,
+// and multiplies them against the resident x with the same per-block matrix
+// instructions and fp32 scaling as the tile kernel. Strip t goes to workgroup
+// t % G and, within it, wavefront (t / G) % 8, so the compute units' shares
+// differ by at most one strip. x rows are stored with 16-byte slot j of row r
+// at j ^ (r & 15) (rows are a multiple of 256 bytes long), so the 16 lanes of
+// each 128-bit operand read hit distinct banks.
+constexpr int kSkWaves = 8;
+constexpr int kSkLdsX = 128 * 1024;           // resident x: 32 RF rows x K values x 2 bytes at most
+
+template <int BITS, int SB>
+struct SkBatch {
+    using CW = typename std::conditional<BITS == 8, u4, u2>::type;    // a lane's codes of one block
+    static constexpr int SV = SB >= 8 ? SB / 8 : 1;                   // loads of the column's SB scales
+    using SW = typename std::conditional<SB >= 8, u4, u2>::type;      // 8 scales (or 4)
+    static_assert(SB >= 4 && (SB == 4 || SB % 8 == 0), "batch size");
+    CW code[SB];
+    SW sc[SV];
+};
+
+template <typename V>
+__device__ __forceinline__ V sk_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (sizeof(V) == 16)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+    else
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+
+template <int BITS, int RF, int SB, int SPS, int P>
+__global__ __launch_bounds__(kSkWaves * 64, 1) void gemm_skinny_kernel(const float *__restrict__ x, int M, int N,
+                                                                       const uint8_t *__restrict__ q,
+                                                                       const uint16_t *__restrict__ s,
+                                                                       float *__restrict__ y)
+{
+    constexpr int BM = 32 * RF;
+    constexpr int C = SB * SPS;                  // blocks per row
+    constexpr int K = 32 * C;
+    constexpr int ROWB = K * 2;                  // bytes of a resident x row
+    constexpr int QROW = K * BITS / 8;           // bytes of a column's codes
+    constexpr int BPB = 32 * BITS / 8;           // code bytes per block and column
+    constexpr int CB = BPB / 2;                  // ... per lane half
+    static_assert(BM * ROWB <= kSkLdsX && ROWB % 256 == 0, "resident x");
+    static_assert(SPS % P == 0, "batch ring slots repeat every strip");
+    using B = SkBatch<BITS, SB>;
+    // Row r = 32 i + c of x is stored as LDS row RF c + i, so the row fragments
+    // of one lane are ROWB bytes apart (an immediate offset of the read).
+    __shared__ __attribute__((aligned(16))) uint8_t lds[BM * ROWB + BM * 4];
+    float *R = reinterpret_cast<float *>(lds + BM * ROWB);
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int c = lane & 31, g = lane >> 5;
+    const int G = gridDim.x;
+    const int strips = (N + 31) >> 5;
+    const int first = (int)blockIdx.x + wv * G, step = kSkWaves * G;
+    const int my = first < strips ? (strips - first + step - 1) / step : 0;   // strips of this wavefront
+
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q, (uint64_t)N * QROW);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint64_t)N * C * 2);
+    auto col_of = [&](int j) {                   // column of this lane in strip j (clamped: loads stay in range)
+        const int n = (first + j * step) * 32 + c;
+        return n < N ? n : N - 1;
+    };
+    auto load = [&](B &b, int ncl, int seg) {    // batch seg of the strip holding column ncl
+        const uint32_t vq = (uint32_t)ncl * QROW + (uint32_t)g * CB;
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb)
+            b.code[kb] = sk_load<typename B::CW>(qr, vq + kb * BPB, (uint32_t)seg * SB * BPB);
+#pragma unroll
+        for (int v = 0; v < B::SV; ++v)
+            b.sc[v] = sk_load<typename B::SW>(sr, (uint32_t)ncl * C * 2 + v * 16, (uint32_t)seg * SB * 2);
+    };
+
+    // The first batches of this wavefront's first strip, then as many stores as
+    // a strip's end issues, all dropped (past the resource): the loop is then
+    // entered with the same memory operations in flight, in the same order, as
+    // it is re-entered from a strip's end, and the wait counts derived for it
+    // keep the later batches in flight.
+    const uint32_t ybytes = (uint32_t)M * (uint32_t)N * 4;
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, ybytes);
+    B ring[P];
+    {
+        const int n0 = col_of(0);
+#pragma unroll
+        for (int p = 0; p < P - 1; ++p) load(ring[p], n0, p);
+#pragma unroll
+        for (int i = 0; i < RF * 16; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(0u, yr, ybytes + (uint32_t)i * N * 4, 0, kNonTemporal);
+    }
+
+    // ---- resident x: wavefront wv prepares rows wv + 8 t (all of their loads in
+    // flight together), with the scaling and operand order of xprep_kernel; rows
+    // past M are zeros
+    {
+        constexpr int RPW = BM / kSkWaves;       // rows per wavefront
+        constexpr int XGS = K / 512;             // groups of 8 values per lane and row
+        static_assert(XGS >= 1 && K % 512 == 0, "x rows are whole multiples of 64 groups");
+        f4 va[RPW][XGS], vb[RPW][XGS];
+#pragma unroll
+        for (int t = 0; t < RPW; ++t) {
+            const int r = wv + kSkWaves * t;
+            const float *xr = x + (size_t)(r < M ? r : 0) * K;
+#pragma unroll
+            for (int i = 0; i < XGS; ++i) {
+                const int qg = lane + 64 * i;
+                va[t][i] = *reinterpret_cast<const f4 *>(xr + 8 * qg);
+                vb[t][i] = *reinterpret_cast<const f4 *>(xr + 8 * qg + 4);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < RPW; ++t) {
+            const int r = wv + kSkWaves * t;
+            uint8_t *row = lds + ((r & 31) * RF + (r >> 5)) * ROWB;
+            const int key = r & 15;
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < XGS; ++i) amax = fmaxf(amax, absmax8(va[t][i], vb[t][i]));
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const int e = row_exponent(amax);
+            const bool live = r < M;
+#pragma unroll
+            for (int i = 0; i < XGS; ++i) {
+                const int qg = lane + 64 * i;
+                const h8 hv = live ? xprep_group<BITS == 8 ? 1 : 0>(va[t][i], vb[t][i], e) : h8{};
+                *reinterpret_cast<h8 *>(row + ((xprep_slot(qg) ^ key) << 4)) = hv;
+            }
+            if (lane == 0) R[r] = live ? ldexpf(1.0f, -e) : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    // ---- per-lane LDS offsets: slot (4 (blk & 3) + 2 st + g) ^ (c & 15) of the lane's row
+    uint32_t aoff[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)                  // u = 2 (blk & 3) + st
+        aoff[u] = (uint32_t)(c * RF) * ROWB + (uint32_t)((((u >> 1) * 4 + (u & 1) * 2 + g) ^ (c & 15)) << 4);
+    const DecodeConsts dc = DecodeConsts::make();
+    const f16v zero = {};
+    f16v acc[RF];
+#pragma unroll
+    for (int i = 0; i < RF; ++i) acc[i] = zero;
+
+    auto compute = [&](const B &b, int seg) {
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb) {
+            const int blk = seg * SB + kb;       // constant after unrolling
+            h8 w0, w1;
+            if constexpr (BITS == 8) {
+                w0 = unpack8_int8(b.code[kb].x, b.code[kb].y, dc);
+                w1 = unpack8_int8(b.code[kb].z, b.code[kb].w, dc);
+            } else {
+                w0 = unpack8_int4(b.code[kb].x, dc);
+                w1 = unpack8_int4(b.code[kb].y, dc);
+            }
+            const uint32_t sw = b.sc[kb >> 3][(kb >> 1) & 3];
+            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (kb & 1))));
+            const uint32_t bo = (uint32_t)(blk & ~3) * 64;
+            const int u = 2 * (blk & 3);
+#pragma unroll
+            for (int i = 0; i < RF; ++i) {
+                const h8 a0 = *reinterpret_cast<const h8 *>(lds + aoff[u] + i * ROWB + bo);
+                const h8 a1 = *reinterpret_cast<const h8 *>(lds + aoff[u + 1] + i * ROWB + bo);
+                f16v p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, w0, zero, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, w1, p, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][v] = __builtin_fmaf(sc, p[v], acc[i][v]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded live ranges
+        }
+    };
+
+    // Output (r, n) is at byte (r N + n) 4 of yr: the lane's part (4 g rows and
+    // its column; past N the resource size) plus the rest of the row, both in
+    // the vector offset, which alone is range-checked: rows past M and columns
+    // past N land past the resource and are dropped.
+    for (int j = 0; j < my; ++j) {
+        const int ncl = col_of(j);
+        const int nxt = col_of(j + 1 < my ? j + 1 : j);
+#pragma unroll
+        for (int sg = 0; sg < SPS; ++sg) {
+            const int ts = sg + P - 1;        // the batch issued now: ts of this strip or ts - SPS of the next
+            if (ts < SPS) load(ring[ts % P], ncl, ts);
+            else load(ring[ts % P], nxt, ts - SPS);
+            compute(ring[sg % P], sg);
+        }
+        const int n = (first + j * step) * 32 + c;
+        const uint32_t lane_off = n < N ? (uint32_t)(4 * g * N + n) * 4 : ybytes;
+#pragma unroll
+        for (int i = 0; i < RF; ++i) {
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const int rg = i * 32 + 8 * j4;  // rows rg + 4 g .. rg + 4 g + 3
+                const f4 f = *reinterpret_cast<const f4 *>(R + rg + 4 * g);
+                const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[i][4 * j4 + v] * fv[v]), yr,
+                                                          lane_off + (uint32_t)(rg + v) * N * 4, 0, kNonTemporal);
+            }
+            acc[i] = zero;
+        }
+    }
+    wait_vm<0>();                                // the batches loaded past the last strip
+}
+
+template <int BITS, int RF, int SB, int SPS, int P>
+hipError_t launch_skinny(const float *x, int64_t M, int64_t N, const void *q, const uint16_t *scales, float *y,
+                         hipStream_t stream)
+{
+    const int64_t strips = (N + 31) / 32;
+    const int64_t want = (strips + kSkWaves - 1) / kSkWaves;
+    const int64_t cus = device_cus();
+    const unsigned grid = (unsigned)(want < cus ? want : cus);
+    gemm_skinny_kernel<BITS, RF, SB, SPS, P><<<grid, kSkWaves * 64, 0, stream>>>(x, (int)M, (int)N,
+                                                                                (const uint8_t *)q, scales, y);
+    return hipGetLastError();
+}
+
 template <int BITS, int BM, int WN, int SK, int NS>
 hipError_t launch_cfg(const _Float16 *x16, const float *rinv, int64_t M, int64_t K, int64_t N, const void *q,
                       const uint16_t *scales, float *y, hipStream_t stream)
@@ -711,9 +954,50 @@ hipError_t gemm_noalloc_scratch(void **ptr)
     return hipSuccess;
 }
 
+bool gemm_skinny(int64_t M, int64_t K, int64_t N, int bits)
+{
+    if ((bits != 4 && bits != 8) || M < 1 || M > 64) return false;
+    if (!(K == 512 || K == 1024 || (K == 2048 && M <= 32))) return false;
+    return (N + 31) / 32 >= 4 * (int64_t)device_cus();      // at least 4 strips per compute unit
+}
+
+// Batches of SB blocks of the strip's 32 columns: kSkSB blocks per batch, up to
+// kSkP batches in registers (one fewer in flight), no more than a strip holds.
+constexpr int kSkSB8 = 4, kSkSB4 = 4;          // blocks per batch: int8, int4
+constexpr int kSkP = 4;
+template <int BITS, int RF, int K>
+hipError_t launch_skinny_kk(const float *x, int64_t M, int64_t N, const void *q, const uint16_t *scales, float *y,
+                            hipStream_t stream)
+{
+    constexpr int SB0 = BITS == 8 ? kSkSB8 : kSkSB4;
+    constexpr int SB = SB0 < K / 32 ? SB0 : K / 32;
+    constexpr int SPS = K / 32 / SB;
+    constexpr int P = SPS < kSkP ? SPS : kSkP;
+    return launch_skinny<BITS, RF, SB, SPS, P>(x, M, N, q, scales, y, stream);
+}
+
+template <int BITS>
+hipError_t launch_skinny_k(const float *x, int64_t M, int64_t K, int64_t N, const void *q, const uint16_t *scales,
+                           float *y, hipStream_t stream)
+{
+    if (K == 512) {
+        if (M <= 32) return launch_skinny_kk<BITS, 1, 512>(x, M, N, q, scales, y, stream);
+        return launch_skinny_kk<BITS, 2, 512>(x, M, N, q, scales, y, stream);
+    }
+    if (K == 1024) {
+        if (M <= 32) return launch_skinny_kk<BITS, 1, 1024>(x, M, N, q, scales, y, stream);
+        return launch_skinny_kk<BITS, 2, 1024>(x, M, N, q, scales, y, stream);
+    }
+    return launch_skinny_kk<BITS, 1, 2048>(x, M, N, q, scales, y, stream);   // M <= 32
+}
+
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits, const void *q,
                        const uint16_t *scales, float *y, void *ws, hipStream_t stream)
 {
+    if (gemm_skinny(M, K, N, bits)) {
+        return bits == 8 ? launch_skinny_k<8>(x, M, K, N, q, scales, y, stream)
+                         : launch_skinny_k<4>(x, M, K, N, q, scales, y, stream);
+    }
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
     float *rinv = reinterpret_cast<float *>((uint8_t *)ws + gemm_ws_x16_bytes(M, K));
     const unsigned pgrid = (unsigned)((M + 3) / 4);

@@ -166,6 +166,9 @@ hipError_t launch_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits
                        const void *q, const uint16_t *scales, float *y, hipStream_t stream);
 hipError_t launch_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
                                int64_t total_tiles, int64_t M, hipStream_t stream);
+// Shapes that run on the skinny GEMM, which prepares x itself: launch_gemm
+// then reads no workspace (ws may be null).
+bool gemm_skinny(int64_t M, int64_t K, int64_t N, int bits);
 // ws: gemm_ws_bytes(M, K) bytes (single call) or the planned workspace (grouped)
 hipError_t launch_gemm(const float *x, int64_t M, int64_t K, int64_t N, int bits,
                        const void *q, const uint16_t *scales, float *y, void *ws, hipStream_t stream);
