@@ -48,6 +48,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak, published
 COPIES = 3                       # rotated package copies (> 4x the 256 MB cache)
 GEMV_SOURCES = ["weight_only_bit_block_amd/csrc/wq_gemv.hip", "weight_only_bit_block_amd/csrc/wq_internal.h",
+                "weight_only_bit_block_amd/csrc/wq_device.h",
                 "weight_only_bit_block_amd/csrc/wq_decode.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_grouped_decode_step_traffic.txt")
 

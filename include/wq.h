@@ -106,8 +106,13 @@ int wq_unpack(const void *q, int64_t N, int64_t K, int bits,
  * (row, block) after a power-of-two normalisation, and the block partials come
  * from fp16 matrix-core instructions with exact products and fp32 sums, then
  * are scaled per block in fp32 as above.
- * Error: |y - y_exact| <= 1e-5 * sum_k |x[m,k]| |w^[n,k]| (M >= 3: for x blocks
- * whose largest magnitude is at least 2^-112).
+ * Error: |y - y_exact| <= 1e-5 * sum_k |x[m,k]| |w^[n,k]| for M <= 2. For
+ * 3 <= M <= 16 the three binary16 parts hold every value within 2^16 of its
+ * (row, block)'s largest magnitude exactly and smaller values with an absolute
+ * error of at most 2^-39 of that largest (2^-151 where it is below 2^-112), so
+ * the bound gains sum_b (2^-39 max_{k in b} |x[m,k]| + 2^-151) sum_{k in b}
+ * |w^[n,k]| over the blocks b of the row; for blocks spread over no more than
+ * 2^16 it is the plain bound.
  */
 int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
             const void *q, const uint16_t *scales, float *y, hipStream_t stream);
@@ -128,10 +133,18 @@ int wq_gemv(const float *x, int64_t M, int64_t K, int64_t N, int bits,
  * The workspace (about 2*M*K bytes) is the calling stream's buffer from the
  * library's pool on the current device (grown when too small; a fresh pool
  * allocation, freed inside the capture, while the stream is being captured).
+ * Few rows and many columns (M <= 64, K = 512 or 1024, or 2048 with M <= 32,
+ * and at least 128 columns per compute unit: the M = 64 lm_head) run as one
+ * kernel instead, which keeps the prepared x (same rounding) in LDS and needs
+ * no workspace.
  * Error: ||Y - Y_exact||_F <= 2e-3 * ||Y_exact||_F per call for finite x whose
- * rows' largest magnitudes are at least 2^-112 (values below 2^-28 of their
- * row's largest magnitude are rounded with an absolute error under 2^-39 of
- * it). A row holding inf or NaN gives non-finite outputs in that row only.
+ * rows' largest magnitudes are at least 2^-112. Elementwise, for any finite x:
+ * |y - y_exact| <= (2^-11 + 1e-5) sum_k |x[m,k]| |w^[n,k]| + 2^-25 2^-e_m
+ * sum_k |w^[n,k]|, where 2^-e_m is row m's scaling (its largest magnitude
+ * times 2^e_m lies in [2^14, 2^15), e_m <= 126): values whose scaled magnitude
+ * is at least 2^-14 keep 11 significant bits, smaller ones an absolute error
+ * of at most 2^-25 scaled. A row holding inf or NaN gives non-finite outputs
+ * in every column of that row and changes no other row.
  * Sizes: M * K * 2, N * K * bits / 8 and N * K / 16 must each be below 2^32,
  * and N below 2^22 (32-bit offsets in the kernels), else WQ_ERR_SHAPE. A pool
  * allocation failure is reported as WQ_ERR_HIP.

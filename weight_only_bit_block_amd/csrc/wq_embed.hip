@@ -16,6 +16,7 @@
 // out, so both sides are coalesced; all 8 values share one block scale.
 // Rows whose id is outside [0, N) are filled with quiet NaN and never read.
 #include "wq_internal.h"
+#include "wq_device.h"
 
 namespace wq {
 namespace {

@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "wq_internal.h"
+#include "wq_device.h"
 #include "wq_decode.h"
 
 namespace wq {
@@ -187,8 +188,13 @@ __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__res
     const wq_desc &d = table[e];
     if (d.N == 0) return;                       // no work, and x may be unset
     const int slot = d.ws_slot;
-    for (int i = 0; i < e; ++i)
-        if (table[i].N > 0 && table[i].ws_slot == slot) return;   // prepared by entry i
+    // earlier entries are checked 64 at a time, one per lane (one load latency)
+    const int lane = threadIdx.x & 63;
+    for (int b0 = 0; b0 < e; b0 += 64) {
+        const int i = b0 + lane;
+        const bool owner = i < e && table[i].N > 0 && table[i].ws_slot == slot;
+        if (__ballot(owner)) return;            // prepared by an earlier entry
+    }
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
     const int K = (int)d.K;
@@ -602,13 +608,25 @@ __global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>
     __shared__ __attribute__((aligned(16))) uint8_t ring[Tile<8, BM, WN, SK, NS, SL>::LDS];
     const int64_t item = blockIdx.x;
     const int tiles_m = (M + BM - 1) / BM;
+    // the entry whose [tile_begin, tile_begin + tiles) holds the item (at most
+    // one does): 64 entries per step, one per lane
+    const int lane = threadIdx.x & 63;
     int e = -1;
-    for (int i = 0; i < count; ++i) {
-        const int64_t tb = table[i].tile_begin;
-        const int64_t tiles = (int64_t)tiles_m * ((table[i].N + 32 * WN - 1) / (32 * WN));
-        if (item >= tb && item < tb + tiles) { e = i; break; }
+    for (int b0 = 0; b0 < count; b0 += 64) {
+        const int i = b0 + lane;
+        bool hit = false;
+        if (i < count) {
+            const int64_t tb = table[i].tile_begin;
+            const int64_t tiles = (int64_t)tiles_m * ((table[i].N + 32 * WN - 1) / (32 * WN));
+            hit = item >= tb && item < tb + tiles;
+        }
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            e = b0 + (int)__builtin_ctzll(m);
+            break;
+        }
     }
-    if (e < 0) return;
+    if (e < 0) return;                           // alignment padding between entries
     const wq_desc &d = table[e];
     const int j = (int)(item - d.tile_begin);
     const int2 tile = make_int2(j % tiles_m, j / tiles_m);

@@ -41,6 +41,7 @@
 // row), far below the depth of ~160 at which fp32 rounding could reach
 // 1e-5 * sum |x||w|.
 #include "wq_internal.h"
+#include "wq_device.h"
 #include "wq_decode.h"
 
 namespace wq {

@@ -110,22 +110,6 @@ __host__ __device__ inline size_t gemv_lds_bytes(int MT, const GemvGeom &g)
 // Upper bound over every shape: nb <= 96 and rows * nb <= 32 * 96 in the fast form.
 __host__ __device__ inline size_t gemv_lds_bytes_max(int MT) { return (size_t)MT * 96 * 128 + 32 * 96 * 2; }
 
-// Workgroup barrier that orders LDS only: waits for this wave's LDS operations,
-// then s_barrier. Unlike __syncthreads() it does not wait for outstanding global
-// loads, so prefetched registers stay in flight across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0); vmcnt and expcnt untouched
-    __builtin_amdgcn_s_barrier();
-}
-
-// Raw buffer descriptor over [p, p + bytes) (bytes < 2^32). Dword 3 selects
-// 32-bit untyped data (raw buffer loads ignore the format otherwise).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)(uint32_t)bytes, 0x00020000);
-}
-
 // ---------------------------------------------------------------- prefill workspace
 // The prefill GEMM rounds x to binary16 once per call (after a per-row
 // power-of-two normalisation) into a workspace: the prepared x [M][K]

@@ -41,6 +41,7 @@
 // factor 2^e is capped at 2^126 so that 2^-e stays a normal fp32 number); any
 // other finite fp32 x is split exactly as above.
 #include "wq_internal.h"
+#include "wq_device.h"
 #include "wq_decode.h"
 
 namespace wq {

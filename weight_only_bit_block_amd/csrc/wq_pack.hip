@@ -14,6 +14,7 @@
 // The library is built with correctly rounded fp32 division and without
 // denormal flushing, so the result is bit-exact.
 #include "wq_internal.h"
+#include "wq_device.h"
 
 namespace wq {
 namespace {
