@@ -145,7 +145,7 @@ int main()
             std::vector<uint8_t> used((size_t)gt, 0);
             for (int i = 0; i < count; ++i) {
                 if (t[i].N == 0) continue;
-                const int64_t n = wq::gemm_grouped_items(M, t[i].N);
+                const int64_t n = wq::gemm_grouped_items(M, t[i].N, t[i].K);
                 EXPECT(t[i].tile_begin % 8 == 0 && t[i].tile_begin + n <= gt);
                 for (int64_t k = 0; k < n && t[i].tile_begin + k < gt; ++k) {
                     EXPECT(!used[(size_t)(t[i].tile_begin + k)]);
@@ -153,6 +153,13 @@ int main()
                 }
             }
             EXPECT(ws % 256 == 0);
+            // the prepared-x slots lie after the split-K header and inside the workspace
+            const uint64_t head = wq::gemm_grouped_header_bytes(M, gt);
+            for (int i = 0; i < count; ++i)
+                if (t[i].N > 0) {
+                    const uint64_t off = (uint64_t)t[i].ws_slot * 256;
+                    EXPECT(off >= head && off + wq::gemm_ws_bytes(M, t[i].K) <= ws);
+                }
         }
         // an inconsistent entry is refused
         if (count > 1) {

@@ -152,14 +152,29 @@ def test_gemm_x_offset_limit(lib):
         assert getattr(lib, fn)(FAKE, 1 << 21, 1024, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
 
 
-def _gemm_items(M, N):
+def _r256(b):
+    return -(-b // 256) * 256
+
+
+def _ksplit(M, K):
+    """Work items per tile: long K loops of short prefills (M <= 128) are split
+    into pieces of about 1024 of K (2 to 8 of them)."""
+    return 1 if M > 128 else max(1, min(8, K // 1024))
+
+
+def _gemm_items(M, N, K):
     bm = 64 if M <= 128 else 128
-    return -(-M // bm) * -(-N // 128)
+    return -(-M // bm) * -(-N // 128) * _ksplit(M, K)
+
+
+def _header(M, items):
+    """Split-K header of the workspace (M <= 128): a flag per item, then a
+    64 x 128 fp32 partial tile per item."""
+    return 0 if M > 128 else _r256(4 * items) + items * 64 * 128 * 4
 
 
 def _ws_bytes(M, K):
-    r = lambda b: -(-b // 256) * 256
-    return r(M * K * 2) + r(M * 4)
+    return _r256(M * K * 2) + _r256(M * 4)
 
 
 @pytest.mark.parametrize("M", [1, 100, 128, 129, 512, 513, 1024, 4096])
@@ -174,19 +189,20 @@ def test_table_plan_gemm(lib, M):
     for i in range(len(specs)):
         arr[i].x, arr[i].y = FAKE + 4096 * i, FAKE
     total, ws = wqa.table_plan_gemm(arr, M)
-    # every entry reads its own x here: one workspace slot each, in table order
-    off = 0
-    for i, (bits, N, K) in enumerate(specs):
-        assert arr[i].ws_slot * 256 == off
-        off += _ws_bytes(M, K)
-    assert ws == off
     order = sorted(range(len(specs)), key=lambda i: (-specs[i][2], i))
     cur = 0
     for i in order:
         cur = -(-cur // 8) * 8
         assert arr[i].tile_begin == cur, (i, arr[i].tile_begin, cur)
-        cur += _gemm_items(M, specs[i][1])
+        cur += _gemm_items(M, specs[i][1], specs[i][2])
     assert total == cur
+    # every entry reads its own x here: one workspace slot each, in table order,
+    # after the split-K header
+    off = _header(M, total)
+    for i, (bits, N, K) in enumerate(specs):
+        assert arr[i].ws_slot * 256 == off
+        off += _ws_bytes(M, K)
+    assert ws == off
 
 
 def test_table_plan_gemm_validation(lib):
@@ -212,7 +228,7 @@ def test_table_plan_gemm_validation(lib):
     assert e.value.status == BITS
     arr[0].bits = 4
     total, ws = wqa.table_plan_gemm(arr, 64)
-    assert total > 0 and ws == _ws_bytes(64, 1024) + _ws_bytes(64, 64)
+    assert total > 0 and ws == _header(64, total) + _ws_bytes(64, 1024) + _ws_bytes(64, 64)
     empty = (W.WqDesc * 0)()
     assert wqa.table_plan_gemm(empty, 64) == (0, 0)
 
@@ -226,7 +242,7 @@ def test_table_plan_gemm_shared_inputs(lib):
     xa, xb = FAKE, FAKE + 4096
     for i, x in enumerate([xa, xa, xa, xa, xb, xa]):
         arr[i].x, arr[i].y = x, FAKE
-    M = 200
+    M = 200                                           # no split-K header above M = 128
     _, ws = wqa.table_plan_gemm(arr, M)
     s = [arr[i].ws_slot for i in range(len(specs))]
     assert s[0] == s[1] == s[3] == 0                  # int4 / int5 order, x_a
@@ -246,6 +262,7 @@ def test_gemm_grouped_validation(lib):
     assert g(FAKE + 16, FAKE, 3, 10, 64, FAKE, 256, None) == ALIGN
     assert g(FAKE, FAKE + 16, 3, 10, 64, FAKE, 256, None) == ALIGN
     assert g(FAKE, FAKE, 3, 10, 64, FAKE + 64, 256, None) == ALIGN
+    assert g(FAKE, FAKE, 3, 10, 64, FAKE, 256, None) == SHAPE     # smaller than the split-K header
     assert g(None, None, 0, 0, 64, None, 0, None) == OK
 
 

@@ -431,13 +431,21 @@ int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tile
             if (d.K != k) continue;
             cur = (cur + wq::kGemmGroupAlign - 1) / wq::kGemmGroupAlign * wq::kGemmGroupAlign;
             d.tile_begin = cur;
-            cur += wq::gemm_grouped_items(M, d.N);
+            cur += wq::gemm_grouped_items(M, d.N, d.K);
             if (cur > (int64_t)0x7FFFFFFF) return WQ_ERR_SHAPE;
         }
         prev = k;
     }
+    // the split-K header (flags and partial tiles) comes first; the slots follow
+    const uint64_t head = wq::gemm_grouped_header_bytes(M, cur);
+    for (int i = 0; i < count; ++i) {
+        if (table[i].N == 0) continue;
+        const uint64_t slot = (uint64_t)table[i].ws_slot + head / wq::kGemmWsUnit;
+        if (slot > (uint64_t)INT32_MAX) return WQ_ERR_SHAPE;
+        table[i].ws_slot = (int32_t)slot;
+    }
     *total_tiles = cur;
-    *workspace_bytes = ws;
+    *workspace_bytes = ws + head;
     return WQ_OK;
 }
 
@@ -453,6 +461,7 @@ int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count, int64
     if (!aligned(base, WQ_TABLE_ALIGN) || !aligned(table_dev, WQ_TABLE_ALIGN) ||
         !aligned(workspace, (uintptr_t)wq::kGemmWsUnit))
         return WQ_ERR_ALIGN;
+    if (workspace_bytes < wq::gemm_grouped_header_bytes(M, total_tiles)) return WQ_ERR_SHAPE;
     return hip_status(wq::launch_gemm_grouped(base, table_dev, count, total_tiles, M, workspace, stream));
 }
 

@@ -182,8 +182,15 @@ __global__ __launch_bounds__(256) void xprep_kernel(const float *__restrict__ x,
 // non-empty entry owns the same workspace slot (entries that share an x and a
 // code order share a slot).
 __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__restrict__ table, int count, int M,
-                                                             uint8_t *__restrict__ ws)
+                                                             uint8_t *__restrict__ ws, int nflags)
 {
+    // clear the split-K flags of this call (the GEMM launch that follows sets them)
+    {
+        uint32_t *flags = reinterpret_cast<uint32_t *>(ws);
+        const int stride = (int)(gridDim.x * gridDim.y) * 256;
+        for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * 256 + (int)threadIdx.x; i < nflags; i += stride)
+            flags[i] = 0u;
+    }
     const int e = blockIdx.y;
     const wq_desc &d = table[e];
     if (d.N == 0) return;                       // no work, and x may be unset
@@ -302,17 +309,48 @@ constexpr int gemm_occupancy() { return WN * SK > 4 ? 1 : (LDS <= 53248 ? 3 : (L
 
 #define WQ_GEMM_BOUNDS(LDS, WN, SK) __launch_bounds__((WN) * (SK) * 64, (gemm_occupancy<LDS, WN, SK>()))
 
+// The K range of a tile's work item and its part in a split across
+// workgroups: stages [st_begin, st_begin + st_count) of the tile's K loop; with
+// P > 1 pieces, piece kp < P - 1 leaves its fp32 partial tile at part + kp BM
+// BN (floats, lane-major) and then sets flag[kp]; piece P - 1 waits for the
+// flags of pieces 0 .. P-2 (workgroups of lower index, dispatched before it),
+// adds their partials in piece order to its own, and stores the tile.
+struct KPiece {
+    int st_begin, st_count, kp, P;
+    float *part;
+    uint32_t *flag;
+};
+
+// Waits (bounded) until a piece's flag is set: device-scope relaxed polls, then
+// one acquire fence; false if it never was (the caller then poisons its tile
+// with NaN, so a broken dispatch-order assumption shows as wrong output, never
+// as a hang).
+__device__ __forceinline__ bool wait_piece(const uint32_t *flag)
+{
+    for (int it = 0; it < (1 << 20); ++it) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    return false;
+}
+
 // The tiles [u = 0, U) of one workgroup, as a stream of K stages: tile_of(u)
 // gives (tm, tn) of the u-th tile. The copies of the next NS - 1 stages are in
 // flight while a stage is computed, across tile boundaries, so a tile's first
 // loads overlap the previous tile's last stages and its stores of y. Every
 // thread of the workgroup calls it, with the same U. ring holds the NS stage
 // buffers of SK * SLICE bytes each.
-template <int BITS, int BM, int WN, int SK, int NS, int SL, class TileOf>
+// ONE: the workgroup has a single tile (U == 1), whose end is handled after
+// the K loop, once every copy has landed; SPLIT: that tile may be a piece of a
+// K loop split across workgroups (kpc.P > 1).
+template <int BITS, int BM, int WN, int SK, int NS, int SL, bool ONE = false, bool SPLIT = false, class TileOf>
 __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, const float *__restrict__ rinv,
                                             int M, int K, int N, const uint8_t *__restrict__ q,
                                             const uint16_t *__restrict__ s, float *__restrict__ y, int U,
-                                            TileOf tile_of, uint8_t *ring)
+                                            TileOf tile_of, uint8_t *ring, KPiece kpc)
 {
     using T = Tile<BITS, BM, WN, SK, NS, SL>;
     using L = typename T::L;
@@ -323,9 +361,9 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
     const int h = wv / WN;                       // K slice
     const int w = wv - h * WN;                   // wavefront within the slice: columns 32w .. 32w+31
     const int C = K >> 5;                        // blocks per row
-    const int NT = (C + KT - 1) / KT;            // stages of the whole K loop
-    const int NTh = (NT + SK - 1) / SK;          // stages of each slice (past K: scale 0)
-    const int st0 = h * NTh;
+    const int NTh = (kpc.st_count + SK - 1) / SK;   // stages of each slice (past the range: scale 0)
+    const int st0 = kpc.st_begin + h * NTh;
+    const int st_end = kpc.st_begin + kpc.st_count;
     const uint32_t qrow = (uint32_t)K * BITS / 8;
     const int c = lane & 31, g = lane >> 5;     // column of the wavefront; lane half
 
@@ -445,7 +483,7 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
             }
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(wb + L::BW + L::HW + (kb * 32 + c) * 4);
             float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> ssh[kb]));
-            sc = (st * KT + kb < C) ? sc : 0.0f;      // blocks past K contribute nothing
+            sc = (st < st_end && st * KT + kb < C) ? sc : 0.0f;   // blocks past the range contribute nothing
             asm volatile("" : "+v"(sc));
             h8 a0[RF], a1[RF];
 #pragma unroll
@@ -492,17 +530,58 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
                 }
             }
         }
-        if (h == 0) {
+        bool store = true;
+        if (SPLIT && kpc.P > 1) {
+            if (kpc.kp < kpc.P - 1) {
+                // a leading piece: its partial, then its flag (after every wavefront's stores)
+                // (the barrier orders every wavefront's stores before thread 0's
+                // device-scope release of the flag)
+                if (h == 0) {
+                    float *dst = kpc.part + (size_t)kpc.kp * BM * BN;
+#pragma unroll
+                    for (int i = 0; i < RF; ++i)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) dst[((i * 16 + v) * WN + w) * 64 + lane] = acc[i][v];
+                }
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(kpc.flag + kpc.kp, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                store = false;
+            } else if (h == 0) {
+                // the last piece: partials of pieces 0 .. P-2 in order, then its own
+                bool ok = true;
+                for (int j = 0; j < kpc.P - 1; ++j) ok = wait_piece(kpc.flag + j) && ok;
+                // one piece at a time, all of its loads in flight together
+                f16v sum[RF];
+                for (int j = 0; j < kpc.P - 1; ++j) {
+                    const float *pj = kpc.part + (size_t)j * BM * BN + w * 64 + lane;
+                    f16v t[RF];
+#pragma unroll
+                    for (int i = 0; i < RF; ++i)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) t[i][v] = pj[(i * 16 + v) * WN * 64];
+#pragma unroll
+                    for (int i = 0; i < RF; ++i) sum[i] = j == 0 ? t[i] : sum[i] + t[i];
+                }
+#pragma unroll
+                for (int i = 0; i < RF; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][v] = ok ? sum[i][v] + acc[i][v] : __builtin_nanf("");
+            }
+        }
+        if (h == 0 && store) {
             const auto tt = tile_of(u);
             const int m0 = tt.x * BM, n0 = tt.y * BN;
             const int rows = M - m0 < BM ? M - m0 : BM;
             const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + (size_t)m0 * N, (uint64_t)rows * N * 4);
             const int n = n0 + w * 32 + c;
             // Output (r, n) of the tile is at byte (r N + n) 4 of yr: a per-lane part
-            // (4 g rows and the column; past N: the resource size) plus the rest of
-            // the row, both in the vector offset, which alone is range-checked:
-            // rows past the tile's last and columns past N land past the resource
-            // and are dropped. (r + rows) N 4 < 2^32 as N < 2^22.
+            // (4 g rows and the column; past N: the resource size) in the vector
+            // offset and the rest of the row in the scalar offset. The buffer range
+            // check covers their sum, so rows past the tile's last and columns past
+            // N land past the resource and are dropped (every kernel's writes are
+            // checked against a guard region by the tests). (r + rows) N 4 < 2^32
+            // as N < 2^22.
             const uint32_t lane_off = n < N ? (uint32_t)(4 * g * N + n) * 4 : (uint32_t)rows * N * 4;
             const uint8_t *R = ring + L::A + L::BW + L::HW + L::SW + 16 * g;   // slice 0's factors
             // 32 x 32 output fragment: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4, column l%32
@@ -516,7 +595,7 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[i][4 * j + v] * fv[v]),
-                                                              yr, lane_off + (uint32_t)(rg + v) * N * 4, 0, kNonTemporal);
+                                                              yr, lane_off, (uint32_t)(rg + v) * N * 4, kNonTemporal);
                 }
             }
         }
@@ -551,18 +630,26 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
         issue(ring + ns * SKS);
         const uint8_t *cur = ring + cs * SKS;
         compute(cur);
-        epi <<= 1;
-        if (++cstl == NTh) {
-            epilogue(cu, cur);
-            epi |= 1;
-            cstl = 0;
-            if (++cu < U) set_scale_halves(cu);
+        if constexpr (ONE) {
+            ++cstl;                              // the single tile ends after the loop
+        } else {
+            epi <<= 1;
+            if (++cstl == NTh) {
+                epilogue(cu, cur);
+                epi |= 1;
+                cstl = 0;
+                if (++cu < U) set_scale_halves(cu);
+            }
         }
         cs = cs + 1 == NS ? 0 : cs + 1;
     }
     // the copies of the stages past the end are still in flight: let them land
-    // before the LDS is released
+    // before the LDS is released (or reused by the end of a single tile)
     wait_vm<0>();
+    if constexpr (ONE) {
+        lds_barrier();
+        epilogue(0, ring);
+    }
 }
 
 // Single call: a persistent grid of G workgroups (a multiple of 8). Workgroup b
@@ -590,7 +677,9 @@ __global__ WQ_GEMM_BOUNDS((Tile<BITS, BM, WN, SK, NS>::LDS), WN, SK) void gemm_k
         const int tm = tt / tiles_n;
         return make_int2(tm, tt - tm * tiles_n);
     };
-    gemm_stream<BITS, BM, WN, SK, NS, Tile<BITS, BM, WN, SK, NS>::SLICE>(x16, rinv, M, K, N, q, s, y, U, tile_of, ring);
+    const KPiece whole = {0, ((K >> 5) + KT - 1) / KT, 0, 1, nullptr, nullptr};
+    gemm_stream<BITS, BM, WN, SK, NS, Tile<BITS, BM, WN, SK, NS>::SLICE>(x16, rinv, M, K, N, q, s, y, U, tile_of, ring,
+                                                                        whole);
 }
 
 // Grouped prefill: the work items of every tensor of a planned table in one
@@ -608,7 +697,7 @@ __global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>
     __shared__ __attribute__((aligned(16))) uint8_t ring[Tile<8, BM, WN, SK, NS, SL>::LDS];
     const int64_t item = blockIdx.x;
     const int tiles_m = (M + BM - 1) / BM;
-    // the entry whose [tile_begin, tile_begin + tiles) holds the item (at most
+    // the entry whose [tile_begin, tile_begin + items) holds the item (at most
     // one does): 64 entries per step, one per lane
     const int lane = threadIdx.x & 63;
     int e = -1;
@@ -617,8 +706,9 @@ __global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>
         bool hit = false;
         if (i < count) {
             const int64_t tb = table[i].tile_begin;
-            const int64_t tiles = (int64_t)tiles_m * ((table[i].N + 32 * WN - 1) / (32 * WN));
-            hit = item >= tb && item < tb + tiles;
+            const int64_t items = (int64_t)tiles_m * ((table[i].N + 32 * WN - 1) / (32 * WN)) *
+                                  gemm_grouped_ksplit(M, table[i].K);
+            hit = item >= tb && item < tb + items;
         }
         const uint64_t m = __ballot(hit);
         if (m) {
@@ -628,21 +718,34 @@ __global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>
     }
     if (e < 0) return;                           // alignment padding between entries
     const wq_desc &d = table[e];
-    const int j = (int)(item - d.tile_begin);
-    const int2 tile = make_int2(j % tiles_m, j / tiles_m);
-    auto tile_of = [&](int) { return tile; };
     const int K = (int)d.K, N = (int)d.N;
+    // item -> tile and piece of its K loop
+    const int P = gemm_grouped_ksplit(M, K);
+    const int j = (int)(item - d.tile_begin);
+    const int t = j / P, kp = j - t * P;
+    const int2 tile = make_int2(t % tiles_m, t / tiles_m);
+    auto tile_of = [&](int) { return tile; };
+    const int NT = ((K >> 5) + KT - 1) / KT;
+    KPiece kpc;
+    kpc.st_begin = kp * NT / P;
+    kpc.st_count = (kp + 1) * NT / P - kpc.st_begin;
+    kpc.kp = kp;
+    kpc.P = P;
+    const int64_t first = d.tile_begin + (int64_t)t * P;      // the tile's first item
+    kpc.flag = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(ws)) + first;
+    kpc.part = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + gemm_grouped_flag_bytes(M, gridDim.x)) +
+               first * (BM * 32 * WN);
     const uint8_t *q = base + d.q_off;
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(base + d.s_off);
     const uint8_t *slot = ws + (size_t)d.ws_slot * kGemmWsUnit;
     const _Float16 *x16 = reinterpret_cast<const _Float16 *>(slot);
     const float *rinv = reinterpret_cast<const float *>(slot + gemm_ws_x16_bytes(M, K));
     if (d.bits == 4)
-        gemm_stream<4, BM, WN, SK, NS, SL>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring);
+        gemm_stream<4, BM, WN, SK, NS, SL, true, BM == 64>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring, kpc);
     else if (d.bits == 5)
-        gemm_stream<5, BM, WN, SK, NS, SL>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring);
+        gemm_stream<5, BM, WN, SK, NS, SL, true, BM == 64>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring, kpc);
     else
-        gemm_stream<8, BM, WN, SK, NS, SL>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring);
+        gemm_stream<8, BM, WN, SK, NS, SL, true, BM == 64>(x16, rinv, M, K, N, q, sc, d.y, 1, tile_of, ring, kpc);
 }
 
 // Compute units of the current device (queried once per device).
@@ -1033,7 +1136,8 @@ hipError_t launch_gemm_grouped(const void *base, const wq_desc *table, int count
 {
     static_assert(kGemmTileN == 128, "tile width of every grouped shape");
     dim3 pgrid((unsigned)((M + 3) / 4), (unsigned)count);
-    xprep_grouped_kernel<<<pgrid, 256, 0, stream>>>(table, count, (int)M, (uint8_t *)ws);
+    const int nflags = gemm_grouped_flag_bytes(M, total_tiles) ? (int)total_tiles : 0;
+    xprep_grouped_kernel<<<pgrid, 256, 0, stream>>>(table, count, (int)M, (uint8_t *)ws, nflags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int bm = gemm_grouped_bm(M), sp = gemm_grouped_split(M);

@@ -131,14 +131,43 @@ static_assert(kGemmNoAllocScratch == WQ_NOALLOC_SCRATCH_BYTES, "wq.h states the 
 // alone: BM-row x 128-column tiles, with the K loop of each tile split over S
 // groups of 256 threads. Short prefills (M <= 128) take 64-row tiles split
 // two ways; longer ones 128-row tiles, unsplit.
+//
+// Short prefills also split long K loops across workgroups, so that every
+// work item covers at most about 1024 of K whatever the tensor's K: a tile of
+// a tensor with K >= 2048 becomes P = min(K / 1024, 8) consecutive work items,
+// item k covering stages [k NT / P, (k + 1) NT / P) of its NT stages. Items
+// 0 .. P-2 leave their fp32 partial tile in the workspace and raise a flag;
+// item P-1 (the highest index of the tile, so it waits only on workgroups
+// dispatched before it) adds the partials in item order to its own, then
+// scales and stores the tile: deterministic, and no read-modify-write atomics.
 constexpr int kGemmTileN = 128;
 constexpr int kGemmGroupAlign = 8;  // entries start at multiples of 8 items (one per XCD)
-inline int gemm_grouped_bm(int64_t M) { return M <= 128 ? 64 : 128; }
-inline int gemm_grouped_split(int64_t M) { return gemm_grouped_bm(M) == 64 ? 2 : 1; }
-inline int64_t gemm_grouped_items(int64_t M, int64_t N)
+constexpr int64_t kGemmKSplitMaxM = 128;
+__host__ __device__ inline int gemm_grouped_bm(int64_t M) { return M <= 128 ? 64 : 128; }
+__host__ __device__ inline int gemm_grouped_split(int64_t M) { return gemm_grouped_bm(M) == 64 ? 2 : 1; }
+__host__ __device__ inline int gemm_grouped_ksplit(int64_t M, int64_t K)
+{
+    if (M > kGemmKSplitMaxM) return 1;
+    const int64_t p = K / 1024;
+    return (int)(p < 1 ? 1 : p > 8 ? 8 : p);
+}
+__host__ __device__ inline int64_t gemm_grouped_items(int64_t M, int64_t N, int64_t K)
 {
     const int bm = gemm_grouped_bm(M);
-    return ((M + bm - 1) / bm) * ((N + kGemmTileN - 1) / kGemmTileN);
+    return ((M + bm - 1) / bm) * ((N + kGemmTileN - 1) / kGemmTileN) * gemm_grouped_ksplit(M, K);
+}
+// Workspace header of a grouped prefill launch of `items` work items, before
+// the prepared-x slots: one 32-bit flag per item (cleared by the preparation
+// kernel of every call), then one fp32 partial tile per item.
+__host__ __device__ inline uint64_t gemm_grouped_flag_bytes(int64_t M, int64_t items)
+{
+    return M > kGemmKSplitMaxM ? 0 : gemm_ws_round((uint64_t)items * 4);
+}
+__host__ __device__ inline uint64_t gemm_grouped_header_bytes(int64_t M, int64_t items)
+{
+    return M > kGemmKSplitMaxM ? 0
+                               : gemm_grouped_flag_bytes(M, items) +
+                                     (uint64_t)items * gemm_grouped_bm(M) * kGemmTileN * 4;
 }
 
 // ---------------------------------------------------------------- launchers
