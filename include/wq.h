@@ -196,9 +196,12 @@ int wq_embed(const int32_t *ids, int64_t n_ids, int64_t K, int64_t N, int bits,
  */
 typedef struct wq_desc {
     int32_t bits;          /* 4, 5 or 8 */
-    int32_t ws_slot;       /* prefill plans: offset of this entry's prepared x in the
-                              grouped workspace, in 256-byte units (set by
-                              wq_table_plan_gemm); decode plans set it to 0 */
+    int32_t ws_slot;       /* prefill plans (set by wq_table_plan_gemm): the offset
+                              of this entry's prepared x in the grouped workspace,
+                              in 256-byte units, when this entry prepares it, or
+                              its bitwise complement (a negative value) when an
+                              earlier entry reading the same x prepares it;
+                              decode plans set it to 0 */
     int64_t N;             /* output features (rows of q) */
     int64_t K;             /* input features, multiple of 32 */
     uint64_t q_off;        /* byte offset of q from the package base, multiple of 64 */
@@ -242,7 +245,11 @@ int wq_gemv_grouped(const void *base, const wq_desc *table_dev, int count,
  * Work items are dispatched longest K first (ties in table order), and each
  * entry's items start at a multiple of 8. Entries that read the same x (same
  * pointer and K) with the same code order (int8, or int4/int5) share one
- * workspace slot. The tile shape depends on M only, so a plan is valid for
+ * workspace slot, prepared by the first of them. For M <= 128 each tile of an
+ * entry with K >= 2048 is min(K / 1024, 8) work items (pieces of its K loop),
+ * and the workspace starts with a header of one 32-bit flag per work item
+ * (rounded up to 256 bytes) and one 64 x 128 fp32 partial tile per work item.
+ * The tile shape and split depend on M and K only, so a plan is valid for
  * exactly the M it was made with.
  */
 int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tiles,
@@ -258,11 +265,20 @@ int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tile
  * planned workspace_bytes, 256-byte aligned (it may be null when that is 0).
  * Each call's y [M][N] is computed as wq_gemm computes it (same preparation of
  * x, unpack and per-block fp32 scaling), with one tile shape for the whole
- * launch: 64-row tiles with each tile's K loop split two ways for M <= 128,
- * 128-row tiles above. The result is deterministic and meets wq_gemm's error
- * bound; it equals wq_gemm bitwise when both use the same tile shape. The
+ * launch: 64-row tiles with each tile's K loop split two ways within the
+ * workgroup for M <= 128, 128-row tiles above. For M <= 128 the K loops of
+ * 2048 and more are also split across workgroups (see wq_table_plan_gemm): the
+ * leading pieces leave their fp32 partials in the workspace and set a flag
+ * with device-scope release ordering; the last piece of the tile, a workgroup
+ * of higher index, waits for those flags (a bounded wait: if a flag never
+ * comes, that tile's outputs are NaN), adds the partials in piece order to its
+ * own and stores y. Nothing is accumulated with atomic read-modify-write
+ * operations. The result is deterministic and meets wq_gemm's error bound; it
+ * equals wq_gemm bitwise when both use the same tile shape and no split. The
  * calls must be independent (no call reads another call's y, the y of
- * different entries do not overlap, and no y overlaps the workspace).
+ * different entries do not overlap, and no y overlaps the workspace); the
+ * workspace must be at least the split-K header of total_tiles work items
+ * (else WQ_ERR_SHAPE).
  */
 int wq_gemm_grouped(const void *base, const wq_desc *table_dev, int count,
                     int64_t total_tiles, int64_t M, void *workspace,

@@ -95,7 +95,7 @@ int main()
     EXPECT(wq_embed(reinterpret_cast<const int32_t *>(FAKE), 3, 33, 8, 8, FQ, FS, FAKE, nullptr) == WQ_ERR_SHAPE);
     EXPECT(wq_embed(nullptr, 0, 32, 8, 8, nullptr, nullptr, nullptr, nullptr) == WQ_OK);
     for (int st = 0; st <= 9; ++st) EXPECT(wq_strerror(st) != nullptr && std::strlen(wq_strerror(st)) > 0);
-    EXPECT(wq_abi_version() == 6);
+    EXPECT(wq_abi_version() == 7);
 
     // layout and planners over random tables
     for (int trial = 0; trial < 200; ++trial) {
@@ -134,13 +134,21 @@ int main()
         const int st = wq_table_plan_gemm(t.data(), count, M, &gt, &ws);
         EXPECT(st == WQ_OK);
         if (st == WQ_OK) {
-            // entries with the same (x, K, int8 order) share a workspace slot; others get distinct ones
-            for (int i = 0; i < count; ++i)
+            // entries with the same (x, K, int8 order) share a workspace slot; others get
+            // distinct ones; the first entry of a slot prepares it (ws_slot >= 0), later
+            // sharers hold the slot's complement
+            auto slot_of = [](int32_t s) { return s >= 0 ? s : ~s; };
+            for (int i = 0; i < count; ++i) {
+                if (t[i].N == 0) continue;
+                bool earlier = false;
                 for (int j = 0; j < i; ++j) {
-                    if (t[i].N == 0 || t[j].N == 0) continue;
+                    if (t[j].N == 0) continue;
                     const bool same = t[i].x == t[j].x && t[i].K == t[j].K && (t[i].bits == 8) == (t[j].bits == 8);
-                    EXPECT(same == (t[i].ws_slot == t[j].ws_slot));
+                    EXPECT(same == (slot_of(t[i].ws_slot) == slot_of(t[j].ws_slot)));
+                    earlier = earlier || same;
                 }
+                EXPECT(earlier == (t[i].ws_slot < 0));
+            }
             // work items of non-empty entries are disjoint and inside the launch
             std::vector<uint8_t> used((size_t)gt, 0);
             for (int i = 0; i < count; ++i) {
@@ -157,7 +165,7 @@ int main()
             const uint64_t head = wq::gemm_grouped_header_bytes(M, gt);
             for (int i = 0; i < count; ++i)
                 if (t[i].N > 0) {
-                    const uint64_t off = (uint64_t)t[i].ws_slot * 256;
+                    const uint64_t off = (uint64_t)slot_of(t[i].ws_slot) * 256;
                     EXPECT(off >= head && off + wq::gemm_ws_bytes(M, t[i].K) <= ws);
                 }
         }

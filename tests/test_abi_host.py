@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
             "wq_embed", "wq_abi_version", "wq_table_plan_gemm", "wq_gemm_grouped", "wq_gemm_noalloc"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.wq_abi_version() == 6
+    assert lib.wq_abi_version() == 7
 
 
 def test_sizes(lib):
@@ -244,7 +244,10 @@ def test_table_plan_gemm_shared_inputs(lib):
         arr[i].x, arr[i].y = x, FAKE
     M = 200                                           # no split-K header above M = 128
     _, ws = wqa.table_plan_gemm(arr, M)
-    s = [arr[i].ws_slot for i in range(len(specs))]
+    raw = [arr[i].ws_slot for i in range(len(specs))]
+    # the first entry of each slot prepares it (ws_slot >= 0); later sharers hold the complement
+    assert [r >= 0 for r in raw] == [True, False, True, False, True, False]
+    s = [r if r >= 0 else ~r for r in raw]
     assert s[0] == s[1] == s[3] == 0                  # int4 / int5 order, x_a
     assert s[2] == s[5] == _ws_bytes(M, 1024) // 256  # int8 order, x_a
     assert s[4] == 2 * _ws_bytes(M, 1024) // 256      # x_b (K = 3072)

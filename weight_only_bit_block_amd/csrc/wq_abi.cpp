@@ -436,13 +436,22 @@ int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tile
         }
         prev = k;
     }
-    // the split-K header (flags and partial tiles) comes first; the slots follow
+    // the split-K header (flags and partial tiles) comes first; the slots follow.
+    // An entry that shares an earlier entry's slot gets the slot's complement.
     const uint64_t head = wq::gemm_grouped_header_bytes(M, cur);
     for (int i = 0; i < count; ++i) {
         if (table[i].N == 0) continue;
         const uint64_t slot = (uint64_t)table[i].ws_slot + head / wq::kGemmWsUnit;
         if (slot > (uint64_t)INT32_MAX) return WQ_ERR_SHAPE;
         table[i].ws_slot = (int32_t)slot;
+    }
+    for (int i = count - 1; i >= 0; --i) {
+        if (table[i].N == 0) continue;
+        for (int j = 0; j < i; ++j)
+            if (table[j].N > 0 && table[j].ws_slot == table[i].ws_slot) {
+                table[i].ws_slot = ~table[i].ws_slot;
+                break;
+            }
     }
     *total_tiles = cur;
     *workspace_bytes = ws + head;
@@ -481,6 +490,6 @@ const char *wq_strerror(int status)
     }
 }
 
-int wq_abi_version(void) { return 6; }
+int wq_abi_version(void) { return 7; }
 
 }  // extern "C"

@@ -52,6 +52,7 @@
 // XCD's L2; y is written with non-temporal stores, scaled by the row's 2^-e_m.
 // The grouped form runs the tiles of every tensor of a planned table in one
 // launch (the projections of a layer), with the same tile body.
+#include <cstddef>
 #include <mutex>
 #include <type_traits>
 
@@ -179,8 +180,8 @@ __global__ __launch_bounds__(256) void xprep_kernel(const float *__restrict__ x,
 }
 
 // Grouped: entry e (blockIdx.y) prepares its x unless it is empty or an earlier
-// non-empty entry owns the same workspace slot (entries that share an x and a
-// code order share a slot).
+// entry owns the same workspace slot (ws_slot < 0: entries that share an x and
+// a code order share a slot).
 __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__restrict__ table, int count, int M,
                                                              uint8_t *__restrict__ ws, int nflags)
 {
@@ -191,17 +192,9 @@ __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__res
         for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * 256 + (int)threadIdx.x; i < nflags; i += stride)
             flags[i] = 0u;
     }
-    const int e = blockIdx.y;
-    const wq_desc &d = table[e];
-    if (d.N == 0) return;                       // no work, and x may be unset
+    const wq_desc &d = table[blockIdx.y];
+    if (d.N == 0 || d.ws_slot < 0) return;      // no work (x may be unset), or prepared by another entry
     const int slot = d.ws_slot;
-    // earlier entries are checked 64 at a time, one per lane (one load latency)
-    const int lane = threadIdx.x & 63;
-    for (int b0 = 0; b0 < e; b0 += 64) {
-        const int i = b0 + lane;
-        const bool owner = i < e && table[i].N > 0 && table[i].ws_slot == slot;
-        if (__ballot(owner)) return;            // prepared by an earlier entry
-    }
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
     const int K = (int)d.K;
@@ -698,26 +691,50 @@ __global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>
     const int64_t item = blockIdx.x;
     const int tiles_m = (M + BM - 1) / BM;
     // the entry whose [tile_begin, tile_begin + items) holds the item (at most
-    // one does): 64 entries per step, one per lane
+    // one does): 64 entries per step, one per lane, each lane reading its whole
+    // descriptor, so that the one found is broadcast from registers (no second
+    // round trip to the table)
     const int lane = threadIdx.x & 63;
-    int e = -1;
+    int e = -1, src = 0;
+    u4 dd[4];
     for (int b0 = 0; b0 < count; b0 += 64) {
         const int i = b0 + lane;
         bool hit = false;
         if (i < count) {
-            const int64_t tb = table[i].tile_begin;
-            const int64_t items = (int64_t)tiles_m * ((table[i].N + 32 * WN - 1) / (32 * WN)) *
-                                  gemm_grouped_ksplit(M, table[i].K);
+            const u4 *pd = reinterpret_cast<const u4 *>(table + i);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dd[k] = pd[k];
+            const int64_t tb = (int64_t)(((uint64_t)dd[3].w << 32) | dd[3].z);
+            const int64_t n = (int64_t)(((uint64_t)dd[0].w << 32) | dd[0].z);
+            const int64_t kk = (int64_t)(((uint64_t)dd[1].y << 32) | dd[1].x);
+            const int64_t items = (int64_t)tiles_m * ((n + 32 * WN - 1) / (32 * WN)) * gemm_grouped_ksplit(M, kk);
             hit = item >= tb && item < tb + items;
         }
         const uint64_t m = __ballot(hit);
         if (m) {
-            e = b0 + (int)__builtin_ctzll(m);
+            src = (int)__builtin_ctzll(m);
+            e = b0 + src;
             break;
         }
     }
     if (e < 0) return;                           // alignment padding between entries
-    const wq_desc &d = table[e];
+    static_assert(offsetof(wq_desc, ws_slot) == 4 && offsetof(wq_desc, N) == 8 && offsetof(wq_desc, K) == 16 &&
+                      offsetof(wq_desc, q_off) == 24 && offsetof(wq_desc, s_off) == 32 &&
+                      offsetof(wq_desc, x) == 40 && offsetof(wq_desc, y) == 48 && offsetof(wq_desc, tile_begin) == 56,
+                  "descriptor dwords decoded below");
+    auto rl = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, src); };
+    auto rl64 = [&](uint32_t lo, uint32_t hi) { return ((uint64_t)rl(hi) << 32) | rl(lo); };
+    wq_desc dl;
+    dl.bits = (int32_t)rl(dd[0].x);
+    dl.ws_slot = (int32_t)rl(dd[0].y);
+    dl.N = (int64_t)rl64(dd[0].z, dd[0].w);
+    dl.K = (int64_t)rl64(dd[1].x, dd[1].y);
+    dl.q_off = rl64(dd[1].z, dd[1].w);
+    dl.s_off = rl64(dd[2].x, dd[2].y);
+    dl.x = reinterpret_cast<const float *>(rl64(dd[2].z, dd[2].w));
+    dl.y = reinterpret_cast<float *>(rl64(dd[3].x, dd[3].y));
+    dl.tile_begin = (int64_t)rl64(dd[3].z, dd[3].w);
+    const wq_desc &d = dl;
     const int K = (int)d.K, N = (int)d.N;
     // item -> tile and piece of its K loop
     const int P = gemm_grouped_ksplit(M, K);
@@ -737,7 +754,7 @@ __global__ WQ_GEMM_BOUNDS((Tile<8, BM, WN, SK, NS, slice_bytes<stage_max<BM, WN>
                first * (BM * 32 * WN);
     const uint8_t *q = base + d.q_off;
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(base + d.s_off);
-    const uint8_t *slot = ws + (size_t)d.ws_slot * kGemmWsUnit;
+    const uint8_t *slot = ws + (size_t)(d.ws_slot < 0 ? ~d.ws_slot : d.ws_slot) * kGemmWsUnit;
     const _Float16 *x16 = reinterpret_cast<const _Float16 *>(slot);
     const float *rinv = reinterpret_cast<const float *>(slot + gemm_ws_x16_bytes(M, K));
     if (d.bits == 4)
