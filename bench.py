@@ -619,7 +619,10 @@ def layer_prefill_leg(torch, wqa, inputs, np, oracle, flush, reps):
             pkg.pack_into(i, torch.from_numpy(w).cuda())
             cols = np.sort(rng.choice(t.N, size=64, replace=False))
             samples.append((cols, w[cols].copy()))
-        xs = [torch.from_numpy(wl.x_for(t)).cuda() for t in wl.tensors]
+        # projections that read one activation in a layer (q, k, v; gate, up) get the same tensor,
+        # so the grouped launch prepares it once
+        xd = {k: torch.from_numpy(wl.activation(k)).cuda() for k in wl.acts}
+        xs = [xd[t.act] for t in wl.tensors]
         ys = [torch.full((M, t.N), float("nan"), dtype=torch.float32, device="cuda") for t in wl.tensors]
         call = wqa.GroupedCall(pkg, xs, ys, M, prefill=True)
         g = cold_ms(torch, call, flush, reps)

@@ -31,7 +31,8 @@
  *     device (created on first use, kept until the process ends) and, per
  *     (device, stream), the workspace of the last call on that stream, reused
  *     while large enough (calls on one stream run in order; streams are told
- *     apart by their process-unique id). No other entry point allocates.
+ *     apart by their process-unique id), and the fixed device scratch of
+ *     wq_gemm_noalloc. No other entry point allocates.
  *   - Arguments are validated on the host before any launch; a non-zero
  *     wq_status is returned and nothing is launched. Requirements: bits in
  *     {4, 5, 8}; K > 0 and K % 32 == 0 (K % 128 == 0 for int5, so rows stay
@@ -41,7 +42,9 @@
  *   - Empty calls (M == 0 or N == 0) return WQ_OK without launching.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); a
  *     launch error is reported as WQ_ERR_HIP. There is no implicit sync.
- *   - Results are deterministic: no atomics, a fixed reduction order.
+ *   - Results are deterministic: no read-modify-write atomics, a fixed
+ *     reduction order (split K loops of the grouped prefill hand partial sums
+ *     over through flag stores and loads and add them in piece order).
  */
 #ifndef WQ_H
 #define WQ_H
