@@ -271,9 +271,9 @@ int wq_table_plan_gemm(wq_desc *table, int count, int64_t M, int64_t *total_tile
  * launch: 64-row tiles with each tile's K loop split two ways within the
  * workgroup for M <= 128, 128-row tiles above. For M <= 128 the K loops of
  * 2048 and more are also split across workgroups (see wq_table_plan_gemm): the
- * leading pieces leave their fp32 partials in the workspace and set a flag
- * with device-scope release ordering; the last piece of the tile, a workgroup
- * of higher index, waits for those flags (a bounded wait: if a flag never
+ * leading pieces leave their fp32 partials in the workspace and then set a
+ * flag, both with device-scope coherent stores; the last piece of the tile, a
+ * workgroup of higher index, waits for those flags (a bounded wait: if a flag never
  * comes, that tile's outputs are NaN), adds the partials in piece order to its
  * own and stores y. Nothing is accumulated with atomic read-modify-write
  * operations. The result is deterministic and meets wq_gemm's error bound; it

@@ -534,3 +534,37 @@ def test_gemm_grouped_bitwise_as_single(torch):
         single = to_host(wqa.gemm(xs[i], pkg.q(i), pkg.scales(i), bits))
         assert np.array_equal(first[i], single), i
         assert np.array_equal(to_host(ys[i]), first[i]), i
+
+
+@pytest.mark.parametrize("M", [64, 128])
+def test_gemm_grouped_split_reuses_workspace(torch, M):
+    """K loops split across workgroups (K = 2048, 4096, 8192: 2, 4 and 8
+    pieces) hand their partial tiles over through the same workspace call
+    after call: three calls in a row on new x each time (y refilled with NaN
+    before each), every one within the GEMM bound against the oracle, so no
+    call reads a partial or a flag left by the one before."""
+    specs = [(4, 1024, 2048), (8, 300, 4096), (4, 200, 8192), (4, 130, 1024)]
+    pkg = wqa.Package(specs)
+    refs = []
+    for i, (bits, N, K) in enumerate(specs):
+        q_ref, s_ref = oracle.quantize(_weights(N, K, (44, i)), bits)
+        pkg.q(i).copy_(to_dev(q_ref))
+        pkg.scales(i).copy_(to_dev(s_ref))
+        refs.append((q_ref, s_ref))
+    xs = [torch.empty((M, K), dtype=torch.float32, device="cuda") for (_, _, K) in specs]
+    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for (_, N, _) in specs]
+    call = wqa.GroupedCall(pkg, xs, ys, M, prefill=True)
+    for r in range(3):
+        hx = []
+        for i, (_, _, K) in enumerate(specs):
+            x = inputs.normal((M, K), seed=(45, i, M, r)) * (1.0 + 3 * r)
+            xs[i].copy_(to_dev(x))
+            hx.append(x)
+        for y in ys:
+            y.fill_(float("nan"))
+        note(f"grouped gemm split reuse M={M} call {r} tiles={call.total_tiles}")
+        call()
+        torch.cuda.synchronize()
+        for i, (bits, N, K) in enumerate(specs):
+            y_ref, _ = oracle.matmul(hx[i], refs[i][0], refs[i][1], bits)
+            check_gemm(to_host(ys[i]), y_ref, f"grouped gemm split reuse M={M} call {r} tensor {i}")

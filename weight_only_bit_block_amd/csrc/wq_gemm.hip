@@ -314,17 +314,25 @@ struct KPiece {
     uint32_t *flag;
 };
 
-// Waits (bounded) until a piece's flag is set: device-scope relaxed polls, then
-// one acquire fence; false if it never was (the caller then poisons its tile
-// with NaN, so a broken dispatch-order assumption shows as wrong output, never
-// as a hang).
+// The pieces of a split tile run on different XCDs, whose L2 caches are not
+// kept coherent with each other. Partial tiles and flags are therefore written
+// and read only with device-scope relaxed atomic accesses, which the hardware
+// keeps coherent at device scope by themselves: such a store writes through
+// the XCD's L2 and is complete at device scope once the wavefront's vmcnt has
+// drained, and such a load does not return a line of its own L2. So neither
+// side needs a device-scope fence, whose release writes back and whose acquire
+// invalidates the whole L2 of its XCD (which all other workgroups there then
+// pay for). The producer drains its stores before the workgroup barrier that
+// precedes thread 0's flag store; the consumer issues its partial loads only
+// after it has read every flag set (a compiler barrier keeps them there).
+
+// Waits (bounded) until a piece's flag is set; false if it never was (the
+// caller then poisons its tile with NaN, so a broken dispatch-order assumption
+// shows as wrong output, never as a hang).
 __device__ __forceinline__ bool wait_piece(const uint32_t *flag)
 {
     for (int it = 0; it < (1 << 20); ++it) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            return true;
-        }
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
         __builtin_amdgcn_s_sleep(8);
     }
     return false;
@@ -526,24 +534,28 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
         bool store = true;
         if (SPLIT && kpc.P > 1) {
             if (kpc.kp < kpc.P - 1) {
-                // a leading piece: its partial, then its flag (after every wavefront's stores)
-                // (the barrier orders every wavefront's stores before thread 0's
-                // device-scope release of the flag)
+                // a leading piece: its partial, then its flag, once every
+                // wavefront's partial stores have completed
                 if (h == 0) {
                     float *dst = kpc.part + (size_t)kpc.kp * BM * BN;
 #pragma unroll
                     for (int i = 0; i < RF; ++i)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) dst[((i * 16 + v) * WN + w) * 64 + lane] = acc[i][v];
+                        for (int v = 0; v < 16; ++v)
+                            __hip_atomic_store(dst + ((i * 16 + v) * WN + w) * 64 + lane, acc[i][v], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    asm volatile("" ::: "memory");
+                    wait_vm<0>();
                 }
                 __syncthreads();
                 if (threadIdx.x == 0)
-                    __hip_atomic_store(kpc.flag + kpc.kp, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(kpc.flag + kpc.kp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 store = false;
             } else if (h == 0) {
                 // the last piece: partials of pieces 0 .. P-2 in order, then its own
                 bool ok = true;
                 for (int j = 0; j < kpc.P - 1; ++j) ok = wait_piece(kpc.flag + j) && ok;
+                asm volatile("" ::: "memory");
                 // one piece at a time, all of its loads in flight together
                 f16v sum[RF];
                 for (int j = 0; j < kpc.P - 1; ++j) {
@@ -552,7 +564,9 @@ __device__ __forceinline__ void gemm_stream(const _Float16 *__restrict__ x16, co
 #pragma unroll
                     for (int i = 0; i < RF; ++i)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) t[i][v] = pj[(i * 16 + v) * WN * 64];
+                        for (int v = 0; v < 16; ++v)
+                            t[i][v] = __hip_atomic_load(pj + (i * 16 + v) * WN * 64, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
                     for (int i = 0; i < RF; ++i) sum[i] = j == 0 ? t[i] : sum[i] + t[i];
                 }
