@@ -18,3 +18,34 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def nan_filled_outputs(request, monkeypatch):
+    """In GPU tests, every output the library functions allocate themselves
+    starts as NaN (as the tests' own output tensors do), so an output that a
+    kernel never writes fails its check instead of passing on leftover memory."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import torch
+    import weight_only_bit_block_amd as wqa
+
+    def matmul(fn):
+        def call(x, q, scales, bits, out=None, stream=None):
+            if out is None and isinstance(x, torch.Tensor) and x.dim() == 2 and isinstance(q, torch.Tensor):
+                out = torch.full((x.shape[0], q.shape[0]), float("nan"), dtype=torch.float32, device=x.device)
+            return fn(x, q, scales, bits, out=out, stream=stream)
+        return call
+
+    def embed(fn):
+        def call(ids, q, scales, K, bits, out=None, stream=None):
+            if out is None and isinstance(ids, torch.Tensor):
+                out = torch.full((ids.numel(), K), float("nan"), dtype=torch.float32, device=ids.device)
+            return fn(ids, q, scales, K, bits, out=out, stream=stream)
+        return call
+
+    for name in ("gemv", "gemm", "gemm_noalloc", "linear"):
+        monkeypatch.setattr(wqa, name, matmul(getattr(wqa, name)))
+    monkeypatch.setattr(wqa, "embed", embed(wqa.embed))
+    yield
