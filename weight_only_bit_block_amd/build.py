@@ -36,9 +36,16 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The matrix-core GEMV's matrix instructions write their
+# results to ordinary vector registers: with the compiler's default choice
+# (accumulation registers) every 32 x 32 partial is read back with one move per
+# value before the fp32 block scaling.
+SOURCE_FLAGS = {"wq_mgemv.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -242,6 +242,10 @@ __device__ __forceinline__ void store_x(const XStage<SB> &xs, int M, uint8_t *bu
         const int idx = t + i * 256;
         const int m = idx / (SB * 4);
         const int blk = (idx / 4) % SB, q = idx & 3;
+        // rows past M are neither split nor stored (their operand rows feed
+        // outputs that are never stored); the 4 lanes of a (row, block) skip
+        // together, and so does a wavefront whose 4 rows all lie past M
+        if (m >= M) continue;
         const float v[8] = {xs.v[i][0].x, xs.v[i][0].y, xs.v[i][0].z, xs.v[i][0].w,
                             xs.v[i][1].x, xs.v[i][1].y, xs.v[i][1].z, xs.v[i][1].w};
         float mx = 0.0f;
@@ -268,15 +272,13 @@ __device__ __forceinline__ void store_x(const XStage<SB> &xs, int M, uint8_t *bu
             p2[operand_slot<BITS>(k)] = h2;
             p3[operand_slot<BITS>(k)] = h3;
         }
-        if (m < M) {
-            const int s = blk * 4 + q;
-            uint8_t *op = buf + (m >> 3) * A::OP_BYTES;
-            const int mm = m & 7;
-            *reinterpret_cast<h8 *>(op + aoff<SB>(mm, s)) = p1;
-            *reinterpret_cast<h8 *>(op + aoff<SB>(8 + mm, s)) = p2;
-            *reinterpret_cast<h8 *>(op + aoff<SB>(16 + mm, s)) = p3;
-            if (q == 0) E[blk * 16 + m] = __builtin_ldexpf(1.0f, -e);
-        }
+        const int s = blk * 4 + q;
+        uint8_t *op = buf + (m >> 3) * A::OP_BYTES;
+        const int mm = m & 7;
+        *reinterpret_cast<h8 *>(op + aoff<SB>(mm, s)) = p1;
+        *reinterpret_cast<h8 *>(op + aoff<SB>(8 + mm, s)) = p2;
+        *reinterpret_cast<h8 *>(op + aoff<SB>(16 + mm, s)) = p3;
+        if (q == 0) E[blk * 16 + m] = __builtin_ldexpf(1.0f, -e);
     }
 }
 
