@@ -959,7 +959,10 @@ __global__ __launch_bounds__(kSkWaves * 64, 1) void gemm_skinny_kernel(const flo
                 w1 = unpack8_int4(b.code[kb].y, dc);
             }
             const uint32_t sw = b.sc[kb >> 3][(kb >> 1) & 3];
-            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (kb & 1))));
+            float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (kb & 1))));
+            // converted once: otherwise each scaling FMA takes the binary16
+            // scale as a mixed-precision operand, which issues at half rate
+            asm volatile("" : "+v"(sc));
             const uint32_t bo = (uint32_t)(blk & ~3) * 64;
             const int u = 2 * (blk & 3);
 #pragma unroll
