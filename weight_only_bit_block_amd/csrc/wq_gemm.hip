@@ -192,6 +192,7 @@ __global__ __launch_bounds__(256) void xprep_grouped_kernel(const wq_desc *__res
         for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * 256 + (int)threadIdx.x; i < nflags; i += stride)
             flags[i] = 0u;
     }
+    if ((int)blockIdx.y >= count) return;
     const wq_desc &d = table[blockIdx.y];
     if (d.N == 0 || d.ws_slot < 0) return;      // no work (x may be unset), or prepared by another entry
     const int slot = d.ws_slot;
