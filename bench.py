@@ -101,6 +101,9 @@ def parse():
                     help="only the prefill legs, printed as one JSON object (the GEMM counter runs use this)")
     ap.add_argument("--prefill-reps", type=int, default=21,
                     help="cold runs per prefill measurement (median reported)")
+    ap.add_argument("--mixed-only", type=int, default=0, metavar="M",
+                    help="only the mixed decode leg at this M, printed as one JSON object "
+                         "(the matrix-core GEMV counter runs use this)")
     return ap.parse_args()
 
 
@@ -399,12 +402,12 @@ def embed_leg(torch, wqa, wl, pkg, host_w, np, oracle, reps=200):
     return out
 
 
-def mixed_leg(torch, wqa, inputs, np, oracle, steps, warmup):
+def mixed_leg(torch, wqa, inputs, np, oracle, steps, warmup, Ms=(1, 2, 4, 8, 16)):
     """Batched decode over the mixed package (attention int8, MLP int4, lm_head
     int8), one grouped launch per step at M = 1, 2, 4, 8 and 16 (M <= 2 on the
     fp32-FMA kernel, M >= 3 on the matrix cores)."""
     out = {}
-    for M in (1, 2, 4, 8, 16):
+    for M in Ms:
         wl = inputs.decode_step(M, mixed=True)
         pkgs, calls, ys, host_w, _ = build_decode(torch, wqa, wl, COPIES)
         launch_ms, wall_ms = time_grouped(torch, calls, steps, warmup)
@@ -743,6 +746,17 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.mixed_only:
+        import numpy as np
+        import oracle
+        if not 1 <= args.mixed_only <= 16:
+            print("bench: --mixed-only takes 1 <= M <= 16", file=sys.stderr)
+            return 2
+        log(f"mixed decode leg at M={args.mixed_only}")
+        res = mixed_leg(torch, wqa, inputs, np, oracle, args.steps, args.warmup, Ms=(args.mixed_only,))
+        print(json.dumps({"decode_step_mixed": res}), flush=True)
+        return 0
 
     if args.prefill_only:
         import numpy as np
