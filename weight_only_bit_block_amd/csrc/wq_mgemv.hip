@@ -17,7 +17,10 @@
 //    scaled unit). A 32-row matrix operand holds 8 activation rows: h1 of row
 //    m in operand row m, h2 in row 8+m, h3 in row 16+m (rows 24..31 unused);
 //    M > 8 takes a second operand. Codes are exact binary16 integers, every
-//    product is exact and the matrix core sums in fp32.
+//    product is exact and the matrix core sums in fp32. Only the operand rows
+//    that carry data are stored in LDS (3 * MR of them, MR = 4 or 8 rows per
+//    part); the lanes of the other rows read a stored row, and their results
+//    are never used.
 //  * Per block and operand, two chained v_mfma_f32_32x32x16_f16 from a zero
 //    accumulator give P[32 x 32]; operand rows m, 8+m and 16+m land in one lane
 //    (values v, v+4, v+8), so row m's block partial is P[v] + P[v+4] + P[v+8],
@@ -26,9 +29,9 @@
 //    output is about 8 + K/32, far below the ~160 at which fp32 rounding could
 //    reach 1e-5 * sum |x||w|.
 //  * A workgroup of 4 wavefronts owns 128 consecutive weight rows (32 per
-//    wavefront, one matrix column each) for all K, walked in segments of 4
-//    blocks. Each wavefront copies its rows' codes of the next segment from HBM
-//    straight into a wave-private LDS buffer (direct-to-LDS buffer loads of
+//    wavefront, one matrix column each) for all K, walked in segments of SB
+//    blocks (seg_blocks). Each wavefront copies its rows' codes of the next
+//    segment from HBM straight into a wave-private LDS buffer (direct-to-LDS buffer loads of
 //    whole cache lines, no registers), while x of the next segment is loaded
 //    into registers and the current segment is computed; x is then split into
 //    the other of two operand buffers. Lane (n, g) reads codes 16g..16g+15 of
@@ -52,22 +55,32 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-// Blocks per segment: 4 for every code width. With at most 8 activation rows
-// the workgroup's LDS (two operand buffers and two code buffers) is then about
-// 49 KiB and three workgroups share a compute unit; 8-block segments for int4
-// (72 KiB, two workgroups) measured 6-7% slower at M = 4 and 8.
+// Blocks per segment. With one operand a segment copies a whole 128-byte line
+// of each of a wavefront's 32 rows for int4 (8 blocks) and int8 (4 blocks):
+// with 4-block int4 segments (half lines) the mixed decode step at M = 4 took
+// 5% longer and the all-int4 step 7% longer. int5 (80 + 16 bytes per 4
+// blocks) and the two-operand form keep 4 blocks: 8 would raise the kernel's
+// registers past 128 (int5) or the two-operand LDS to 66 KiB.
 template <int BITS, int MF>
-constexpr int seg_blocks() { return 4; }
+constexpr int seg_blocks() { return BITS == 4 && MF == 1 ? 8 : 4; }
 
-// Operand buffer of a segment of SB blocks: MF 32-row operands (binary16, row
-// pitch SB * 64 bytes) and the factors 2^-e, [SB][16] floats.
-template <int MF, int SB>
+// Operand buffer of a segment of SB blocks: MF operands of 3 * MR stored rows
+// (binary16, row pitch SB * 64 bytes) and the factors 2^-e, [SB][16] floats.
+template <int MF, int MR, int SB>
 struct Buf {
     static constexpr int ROW_BYTES = SB * 32 * 2;
-    static constexpr int OP_BYTES = 32 * ROW_BYTES;
+    static constexpr int OP_BYTES = 3 * MR * ROW_BYTES;
     static constexpr int A_BYTES = MF * OP_BYTES;
     static constexpr int BYTES = A_BYTES + 16 * SB * 4;
 };
+
+// Stored row of operand row r (0..31): part r / 8 (h1, h2, h3; 3 is unused),
+// activation row r % 8; rows without data read stored row 0.
+template <int MR>
+__device__ __forceinline__ int stored_row(int r)
+{
+    return ((r >> 3) < 3 && (r & 7) < MR) ? (r >> 3) * MR + (r & 7) : 0;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
@@ -206,19 +219,20 @@ __device__ __forceinline__ Scales<SB> load_scales(__amdgpu_buffer_rsrc_t sr, uin
 }
 
 // x of one segment: group i (8 values) of the segment is row m, block blk,
-// k-group q (i = (m * SB + blk) * 4 + q); a thread holds XG groups (16 rows).
-template <int SB>
+// k-group q (i = (m * SB + blk) * 4 + q); a thread holds XG groups (8 * MF
+// rows; threads past them hold none).
+template <int MF, int SB>
 struct XStage {
-    static constexpr int XG = 16 * SB * 4 / 256;
+    static constexpr int XG = 8 * MF * SB * 4 / 256 > 0 ? 8 * MF * SB * 4 / 256 : 1;
     f4 v[XG][2];
 };
 
-template <int SB>
-__device__ __forceinline__ void load_x(XStage<SB> &xs, const float *__restrict__ x, int M, int K, int b0, int t)
+template <int MF, int SB>
+__device__ __forceinline__ void load_x(XStage<MF, SB> &xs, const float *__restrict__ x, int M, int K, int b0, int t)
 {
     const int C = K >> 5;
 #pragma unroll
-    for (int i = 0; i < XStage<SB>::XG; ++i) {
+    for (int i = 0; i < XStage<MF, SB>::XG; ++i) {
         const int idx = t + i * 256;
         int m = idx / (SB * 4);
         const int blk = (idx / 4) % SB, q = idx & 3;
@@ -232,13 +246,13 @@ __device__ __forceinline__ void load_x(XStage<SB> &xs, const float *__restrict__
 }
 
 // Split the staged x into the operand rows and the per-(row, block) factors.
-template <int BITS, int MF, int SB>
-__device__ __forceinline__ void store_x(const XStage<SB> &xs, int M, uint8_t *buf, int t)
+template <int BITS, int MF, int MR, int SB>
+__device__ __forceinline__ void store_x(const XStage<MF, SB> &xs, int M, uint8_t *buf, int t)
 {
-    using A = Buf<MF, SB>;
+    using A = Buf<MF, MR, SB>;
     float *E = reinterpret_cast<float *>(buf + A::A_BYTES);
 #pragma unroll
-    for (int i = 0; i < XStage<SB>::XG; ++i) {
+    for (int i = 0; i < XStage<MF, SB>::XG; ++i) {
         const int idx = t + i * 256;
         const int m = idx / (SB * 4);
         const int blk = (idx / 4) % SB, q = idx & 3;
@@ -274,20 +288,20 @@ __device__ __forceinline__ void store_x(const XStage<SB> &xs, int M, uint8_t *bu
         }
         const int s = blk * 4 + q;
         uint8_t *op = buf + (m >> 3) * A::OP_BYTES;
-        const int mm = m & 7;
+        const int mm = m & 7;                    // < MR
         *reinterpret_cast<h8 *>(op + aoff<SB>(mm, s)) = p1;
-        *reinterpret_cast<h8 *>(op + aoff<SB>(8 + mm, s)) = p2;
-        *reinterpret_cast<h8 *>(op + aoff<SB>(16 + mm, s)) = p3;
+        *reinterpret_cast<h8 *>(op + aoff<SB>(MR + mm, s)) = p2;
+        *reinterpret_cast<h8 *>(op + aoff<SB>(2 * MR + mm, s)) = p3;
         if (q == 0) E[blk * 16 + m] = __builtin_ldexpf(1.0f, -e);
     }
 }
 
 // One item: weight rows row0 .. row0+127 of one tensor, all M activation rows
-// (M <= 8 * MF). bq: the LDS buffer of the codes (a separate array, so reads of
-// the operand buffers never wait for copies into it). Each wavefront moves its
+// (M <= 8 * (MF - 1) + MR). bq: the LDS buffer of the codes (a separate array,
+// so reads of the operand buffers never wait for copies into it). Each wavefront moves its
 // codes of a segment from bq into registers when the segment starts, so the
 // same buffer then takes the next segment's copies.
-template <int BITS, int MF>
+template <int BITS, int MF, int MR>
 __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, int K, int64_t N,
                                            const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
                                            float *__restrict__ y, int64_t row0, uint8_t *__restrict__ lds,
@@ -297,8 +311,9 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int r = lane & 31, g = lane >> 5;
+    const int ar = stored_row<MR>(r);            // the lane's operand row as stored
     constexpr int SB = seg_blocks<BITS, MF>();
-    using A = Buf<MF, SB>;
+    using A = Buf<MF, MR, SB>;
     using BS = BStage<BITS, SB>;
     const int C = K >> 5;
     const int nseg = (C + SB - 1) / SB;
@@ -322,12 +337,12 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
         for (int v = 0; v < 4; ++v) acc[f][v] = 0.0f;
     const f16v zero = {};
 
-    XStage<SB> xs;
+    XStage<MF, SB> xs;
     Scales<SB> scv = load_scales<SB>(sr, rows, C, 0), scn = scv;
     // prologue: segment 0's codes copied, its x split into buffer 0
     stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, 0, wq, lane);
-    load_x<SB>(xs, x, M, K, 0, t);
-    store_x<BITS, MF, SB>(xs, M, lds, t);
+    load_x<MF, SB>(xs, x, M, K, 0, t);
+    store_x<BITS, MF, MR, SB>(xs, M, lds, t);
     lds_barrier();
 
     // One segment: codes from the buffer into registers, then the next
@@ -346,9 +361,12 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
         asm volatile("" ::: "memory");
         if (more) {
             // next segment: x first (split at the end of this one), then the
-            // scales, then the code copies, which stay in flight the longest
-            load_x<SB>(xs, x, M, K, b0 + SB, t);
-            scn = load_scales<SB>(sr, rows, C, b0 + SB);
+            // code copies, which stay in flight the longest. Its scales: with
+            // one operand they are loaded before this segment's last block,
+            // when the codes of the other blocks no longer hold registers
+            // (128 registers, four wavefronts per SIMD); with two, here.
+            load_x<MF, SB>(xs, x, M, K, b0 + SB, t);
+            if constexpr (MF == 2) scn = load_scales<SB>(sr, rows, C, b0 + SB);
             stage_codes<BITS, SB>(qr, qrow, K, nrow0, N, b0 + SB, wq, lane);
         }
         // A operands and factors one block ahead of their matrix instructions
@@ -357,8 +375,8 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
 #pragma unroll
         for (int f = 0; f < MF; ++f) {
             const uint8_t *op = buf + f * A::OP_BYTES;
-            na0[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, 2 * g));
-            na1[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, 2 * g + 1));
+            na0[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(ar, 2 * g));
+            na1[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(ar, 2 * g + 1));
             nef[f] = *reinterpret_cast<const f4 *>(E + 8 * f + 4 * g);
         }
 #pragma unroll
@@ -372,8 +390,8 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
 #pragma unroll
                 for (int f = 0; f < MF; ++f) {
                     const uint8_t *op = buf + f * A::OP_BYTES;
-                    na0[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, (j + 1) * 4 + 2 * g));
-                    na1[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(r, (j + 1) * 4 + 2 * g + 1));
+                    na0[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(ar, (j + 1) * 4 + 2 * g));
+                    na1[f] = *reinterpret_cast<const h8 *>(op + aoff<SB>(ar, (j + 1) * 4 + 2 * g + 1));
                     nef[f] = *reinterpret_cast<const f4 *>(E + (j + 1) * 16 + 8 * f + 4 * g);
                 }
             }
@@ -396,11 +414,12 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
                     asm volatile("" : "+v"(acc[f][v]));   // the block's scaling happens here
                 }
             }
+            if (MF == 1 && j == SB - 2 && more) scn = load_scales<SB>(sr, rows, C, b0 + SB);
             __builtin_amdgcn_sched_barrier(0);   // keep each block's work together (bounds live registers)
         }
         if (more) {
-            store_x<BITS, MF, SB>(xs, M, lds + ((seg + 1) & 1) * A::BYTES, t);
             scv = scn;
+            store_x<BITS, MF, MR, SB>(xs, M, lds + ((seg + 1) & 1) * A::BYTES, t);
             lds_barrier();                       // the next operand buffer is complete, this one free
         }
     };
@@ -416,27 +435,30 @@ __device__ __forceinline__ void mgemv_item(const float *__restrict__ x, int M, i
     }
 }
 
-template <int BITS, int MF>
+template <int BITS, int MF, int MR>
 __global__ __launch_bounds__(256) void mgemv_kernel(const float *__restrict__ x, int M, int K, int64_t N,
                                                     const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
                                                     float *__restrict__ y)
 {
     constexpr int SB = seg_blocks<BITS, MF>();
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Buf<MF, SB>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Buf<MF, MR, SB>::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t bq[BStage<BITS, SB>::BYTES];
-    mgemv_item<BITS, MF>(x, M, K, N, q, s, y, (int64_t)blockIdx.x * kMgemvRows, lds, bq);
+    mgemv_item<BITS, MF, MR>(x, M, K, N, q, s, y, (int64_t)blockIdx.x * kMgemvRows, lds, bq);
 }
 
-template <int MF>
+template <int A_, int B_>
+constexpr int cmax() { return A_ > B_ ? A_ : B_; }
+
+template <int MF, int MR>
 __global__ __launch_bounds__(256) void mgemv_grouped_kernel(const uint8_t *__restrict__ base,
                                                             const wq_desc *__restrict__ table, int count, int M)
 {
     // buffers sized for the largest of the three code widths
-    constexpr int SB4 = seg_blocks<4, MF>(), SB8 = seg_blocks<8, MF>();
-    constexpr int AB = Buf<MF, SB4>::BYTES > Buf<MF, SB8>::BYTES ? Buf<MF, SB4>::BYTES : Buf<MF, SB8>::BYTES;
-    constexpr int B5 = BStage<5, SB4>::BYTES, B8 = BStage<8, SB8>::BYTES;
+    constexpr int SB4 = seg_blocks<4, MF>(), SB5 = seg_blocks<5, MF>(), SB8 = seg_blocks<8, MF>();
+    constexpr int AB = cmax<cmax<Buf<MF, MR, SB4>::BYTES, Buf<MF, MR, SB5>::BYTES>(), Buf<MF, MR, SB8>::BYTES>();
+    constexpr int BB = cmax<cmax<BStage<4, SB4>::BYTES, BStage<5, SB5>::BYTES>(), BStage<8, SB8>::BYTES>();
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * AB];
-    __shared__ __attribute__((aligned(16))) uint8_t bq[B5 > B8 ? B5 : B8];
+    __shared__ __attribute__((aligned(16))) uint8_t bq[BB];
     const int64_t item = blockIdx.x;
     int lo = 0, hi = count - 1;
     while (lo < hi) {
@@ -447,9 +469,9 @@ __global__ __launch_bounds__(256) void mgemv_grouped_kernel(const uint8_t *__res
     const uint8_t *q = base + d.q_off;
     const uint16_t *s = reinterpret_cast<const uint16_t *>(base + d.s_off);
     const int64_t row0 = (item - d.tile_begin) * kMgemvRows;
-    if (d.bits == 4) mgemv_item<4, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
-    else if (d.bits == 5) mgemv_item<5, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
-    else mgemv_item<8, MF>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
+    if (d.bits == 4) mgemv_item<4, MF, MR>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
+    else if (d.bits == 5) mgemv_item<5, MF, MR>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
+    else mgemv_item<8, MF, MR>(d.x, M, (int)d.K, d.N, q, s, d.y, row0, lds, bq);
 }
 
 }  // namespace
@@ -459,14 +481,20 @@ hipError_t launch_mgemv(const float *x, int64_t M, int64_t K, int64_t N, int bit
 {
     const unsigned grid = (unsigned)((N + kMgemvRows - 1) / kMgemvRows);
     const uint8_t *qb = (const uint8_t *)q;
-    if (M <= 8) {
-        if (bits == 4) mgemv_kernel<4, 1><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
-        else if (bits == 5) mgemv_kernel<5, 1><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
-        else mgemv_kernel<8, 1><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+    // MR: activation rows per operand part stored in LDS (4 keeps the LDS of a
+    // workgroup at 29 KiB, four workgroups per compute unit)
+    if (M <= 4) {
+        if (bits == 4) mgemv_kernel<4, 1, 4><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        else if (bits == 5) mgemv_kernel<5, 1, 4><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        else mgemv_kernel<8, 1, 4><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+    } else if (M <= 8) {
+        if (bits == 4) mgemv_kernel<4, 1, 8><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        else if (bits == 5) mgemv_kernel<5, 1, 8><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        else mgemv_kernel<8, 1, 8><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
     } else {
-        if (bits == 4) mgemv_kernel<4, 2><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
-        else if (bits == 5) mgemv_kernel<5, 2><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
-        else mgemv_kernel<8, 2><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        if (bits == 4) mgemv_kernel<4, 2, 8><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        else if (bits == 5) mgemv_kernel<5, 2, 8><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
+        else mgemv_kernel<8, 2, 8><<<grid, 256, 0, stream>>>(x, (int)M, (int)K, N, qb, scales, y);
     }
     return hipGetLastError();
 }
@@ -474,10 +502,12 @@ hipError_t launch_mgemv(const float *x, int64_t M, int64_t K, int64_t N, int bit
 hipError_t launch_mgemv_grouped(const void *base, const wq_desc *table_dev, int count, int64_t total_items,
                                 int64_t M, hipStream_t stream)
 {
-    if (M <= 8)
-        mgemv_grouped_kernel<1><<<(unsigned)total_items, 256, 0, stream>>>((const uint8_t *)base, table_dev, count, (int)M);
+    if (M <= 4)
+        mgemv_grouped_kernel<1, 4><<<(unsigned)total_items, 256, 0, stream>>>((const uint8_t *)base, table_dev, count, (int)M);
+    else if (M <= 8)
+        mgemv_grouped_kernel<1, 8><<<(unsigned)total_items, 256, 0, stream>>>((const uint8_t *)base, table_dev, count, (int)M);
     else
-        mgemv_grouped_kernel<2><<<(unsigned)total_items, 256, 0, stream>>>((const uint8_t *)base, table_dev, count, (int)M);
+        mgemv_grouped_kernel<2, 8><<<(unsigned)total_items, 256, 0, stream>>>((const uint8_t *)base, table_dev, count, (int)M);
     return hipGetLastError();
 }
 
