@@ -109,28 +109,36 @@ struct BStage {
     __device__ static constexpr int swz(int rr) { return (rr / (16 / SLOTS)) % SLOTS; }
 };
 
+template <int POLICY>
 __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_base, uint32_t off)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, off, 0, 0,
+                                             POLICY);
 }
 
 // Issue the copies of segment b0 .. b0+SB-1 of weight rows nrow0 .. nrow0+31
-// into this wavefront's region dst: each instruction moves 64 / SLOTS whole rows
-// (full cache lines). Reads past the tensor return zeros; blocks past K read
-// the next row's codes, whose scale is taken as 0.
+// into this wavefront's region dst: each instruction moves the segment's part
+// of 64 / SLOTS rows. Reads past the tensor return zeros; blocks past K read
+// the next row's codes, whose scale is taken as 0. Copies of whole 128-byte
+// lines use the non-temporal policy (the codes are read once): with it the
+// mixed decode step at M = 3..8 ran 4-5% faster. Partial lines (int5, int4 in
+// 4-block segments) keep the default policy, which lets the cache serve the
+// rest of the line to the next segment's copies: non-temporal copies of half
+// lines made the step 8% slower.
 template <int BITS, int SB>
 __device__ __forceinline__ void stage_codes(__amdgpu_buffer_rsrc_t qr, uint32_t qrow, int K, int64_t nrow0, int64_t N,
                                             int b0, uint8_t *dst, int lane)
 {
     using B = BStage<BITS, SB>;
     constexpr int RPI = 64 / B::SLOTS;             // rows per instruction
+    constexpr int POL = BITS != 5 && B::ROW % 128 == 0 ? kNonTemporal : 0;
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
         const int rr = i * RPI + lane / B::SLOTS;
         const int p = (lane % B::SLOTS) ^ B::swz(rr);
         int64_t n = nrow0 + rr;
         n = n < N ? n : N - 1;
-        copy16(qr, dst + i * 1024, (uint32_t)n * qrow + (uint32_t)b0 * (B::ROW / SB) + (uint32_t)p * 16);
+        copy16<POL>(qr, dst + i * 1024, (uint32_t)n * qrow + (uint32_t)b0 * (B::ROW / SB) + (uint32_t)p * 16);
     }
     if constexpr (BITS == 5) {
         // the rows' bit-4 dwords: SB / 4 pieces of 16 bytes per row
@@ -139,7 +147,7 @@ __device__ __forceinline__ void stage_codes(__amdgpu_buffer_rsrc_t qr, uint32_t 
         if (rr < 32) {
             int64_t n = nrow0 + rr;
             n = n < N ? n : N - 1;
-            copy16(qr, dst + B::CODE_BYTES, (uint32_t)n * qrow + (uint32_t)K / 2 + (uint32_t)(b0 + 4 * h) * 4);
+            copy16<0>(qr, dst + B::CODE_BYTES, (uint32_t)n * qrow + (uint32_t)K / 2 + (uint32_t)(b0 + 4 * h) * 4);
         }
     }
 }
