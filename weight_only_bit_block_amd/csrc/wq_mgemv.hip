@@ -31,8 +31,8 @@
 //  * A workgroup of 4 wavefronts owns 128 consecutive weight rows (32 per
 //    wavefront, one matrix column each) for all K, walked in segments of SB
 //    blocks (seg_blocks). Each wavefront copies its rows' codes of the next
-//    segment from HBM straight into a wave-private LDS buffer (direct-to-LDS buffer loads of
-//    whole cache lines, no registers), while x of the next segment is loaded
+//    segment from HBM straight into a wave-private LDS buffer (direct-to-LDS
+//    buffer loads, no registers), while x of the next segment is loaded
 //    into registers and the current segment is computed; x is then split into
 //    the other of two operand buffers. Lane (n, g) reads codes 16g..16g+15 of
 //    each block of its row from LDS and unpacks them in registers. The operand
