@@ -877,6 +877,27 @@ __global__ __launch_bounds__(kSkWaves * 64, 1) void gemm_skinny_kernel(const flo
             b.sc[v] = sk_load<typename B::SW>(sr, (uint32_t)ncl * C * 2 + v * 16, (uint32_t)seg * SB * 2);
     };
 
+    // ---- resident x, loads: wavefront wv prepares rows wv + 8 t, all of their
+    // loads in flight together. They are issued before the first code batches:
+    // loads complete in order, so x issued after the batches waited for all of
+    // them (the M=64 lm_head, back to back over rotated copies: 57.0 us that
+    // way, 54.2 us this way).
+    constexpr int RPW = BM / kSkWaves;           // rows per wavefront
+    constexpr int XGS = K / 512;                 // groups of 8 values per lane and row
+    static_assert(XGS >= 1 && K % 512 == 0, "x rows are whole multiples of 64 groups");
+    f4 va[RPW][XGS], vb[RPW][XGS];
+#pragma unroll
+    for (int t = 0; t < RPW; ++t) {
+        const int r = wv + kSkWaves * t;
+        const float *xr = x + (size_t)(r < M ? r : 0) * K;
+#pragma unroll
+        for (int i = 0; i < XGS; ++i) {
+            const int qg = lane + 64 * i;
+            va[t][i] = *reinterpret_cast<const f4 *>(xr + 8 * qg);
+            vb[t][i] = *reinterpret_cast<const f4 *>(xr + 8 * qg + 4);
+        }
+    }
+
     // The first batches of this wavefront's first strip, then as many stores as
     // a strip's end issues, all dropped (past the resource): the loop is then
     // entered with the same memory operations in flight, in the same order, as
@@ -894,25 +915,15 @@ __global__ __launch_bounds__(kSkWaves * 64, 1) void gemm_skinny_kernel(const flo
             __builtin_amdgcn_raw_buffer_store_b32(0u, yr, ybytes + (uint32_t)i * N * 4, 0, kNonTemporal);
     }
 
-    // ---- resident x: wavefront wv prepares rows wv + 8 t (all of their loads in
-    // flight together), with the scaling and operand order of xprep_kernel; rows
-    // past M are zeros
+    // ---- resident x, rounding: the scaling and operand order of xprep_kernel;
+    // rows past M are zeros. The x values pass through an empty asm first, so
+    // no use of them is moved up between their loads (which would wait for the
+    // first row before the other rows' loads are issued).
+#pragma unroll
+    for (int t = 0; t < RPW; ++t)
+#pragma unroll
+        for (int i = 0; i < XGS; ++i) asm volatile("" : "+v"(va[t][i]), "+v"(vb[t][i]));
     {
-        constexpr int RPW = BM / kSkWaves;       // rows per wavefront
-        constexpr int XGS = K / 512;             // groups of 8 values per lane and row
-        static_assert(XGS >= 1 && K % 512 == 0, "x rows are whole multiples of 64 groups");
-        f4 va[RPW][XGS], vb[RPW][XGS];
-#pragma unroll
-        for (int t = 0; t < RPW; ++t) {
-            const int r = wv + kSkWaves * t;
-            const float *xr = x + (size_t)(r < M ? r : 0) * K;
-#pragma unroll
-            for (int i = 0; i < XGS; ++i) {
-                const int qg = lane + 64 * i;
-                va[t][i] = *reinterpret_cast<const f4 *>(xr + 8 * qg);
-                vb[t][i] = *reinterpret_cast<const f4 *>(xr + 8 * qg + 4);
-            }
-        }
 #pragma unroll
         for (int t = 0; t < RPW; ++t) {
             const int r = wv + kSkWaves * t;
