@@ -1059,7 +1059,10 @@ hipError_t launch_cfg(const _Float16 *x16, const float *rinv, int64_t M, int64_t
 //    unpack feeding four row fragments; three workgroups per compute unit with
 //    two stages in flight when that gives no more tiles per compute unit than
 //    two workgroups with three stages (the M = 4096 gate projection: 768 tiles,
-//    one per workgroup, measured 11% faster), else the latter;
+//    one per workgroup, measured 11% faster), else the latter. int5 always
+//    takes the latter: under the register limit of three workgroups (168) its
+//    K loop spills (the bit-4 dwords and their unpack constants), and the
+//    M = 4096 int5 gate projection took 79.8 us cold against 63.2 us with two;
 //  - C .. 2 C such tiles: the same tiles with the K loop of each split over two
 //    wavefront groups of one workgroup;
 //  - fewer: 64-row tiles (the M = 64 int8 lm_head has 1187 of them) with four
@@ -1075,8 +1078,10 @@ hipError_t launch_shape(const _Float16 *x16, const float *rinv, int64_t M, int64
     const int64_t t128 = ((M + 127) / 128) * tn;
     const int64_t t64 = ((M + 63) / 64) * tn;
     if (M > 64 && t128 >= 2 * cus) {
-        const int64_t per3 = 3 * ((t128 + 3 * cus - 1) / (3 * cus)), per2 = 2 * ((t128 + 2 * cus - 1) / (2 * cus));
-        if (per3 <= per2) return launch_cfg<BITS, 128, 4, 1, 2>(x16, rinv, M, K, N, q, scales, y, stream);
+        if constexpr (BITS != 5) {
+            const int64_t per3 = 3 * ((t128 + 3 * cus - 1) / (3 * cus)), per2 = 2 * ((t128 + 2 * cus - 1) / (2 * cus));
+            if (per3 <= per2) return launch_cfg<BITS, 128, 4, 1, 2>(x16, rinv, M, K, N, q, scales, y, stream);
+        }
         return launch_cfg<BITS, 128, 4, 1, 3>(x16, rinv, M, K, N, q, scales, y, stream);
     }
     if (M > 64 && t128 >= cus) return launch_cfg<BITS, 128, 4, 2, 3>(x16, rinv, M, K, N, q, scales, y, stream);
