@@ -122,6 +122,26 @@ def test_gemm_parity_int5(torch, K, N):
                 assert np.linalg.norm(y[m] - y_ref[m]) <= 2e-3 * den, m
 
 
+def test_gemm_int5_long_prefill_shape(torch):
+    """A long int5 prefill (at least 2 C tiles of 128 x 128, K = 1024: the shape
+    that takes two workgroups per compute unit with three stages), with ragged M
+    and N, on sampled columns against the oracle and against the binary16-x
+    diagnostic reference elementwise."""
+    M, K, N = 2100, 1024, 4000
+    cols = np.sort(inputs.generator((71, 1)).choice(N, size=96, replace=False))
+    w = _weights(N, K, (70, K, N))
+    x = inputs.normal((M, K), seed=(72, K, N))
+    x[::97] *= 20
+    q_ref, s_ref = oracle.quantize(w, 5)
+    qs, ss = oracle.quantize(w[cols], 5)
+    y_ref, _ = oracle.matmul(x, qs, ss, 5)
+    y16, B16 = oracle.matmul(x, qs, ss, 5, x16=True)
+    note(f"gemm int5 long prefill M={M} K={K} N={N}")
+    y = to_host(wqa.gemm(to_dev(x), to_dev(q_ref), to_dev(s_ref), 5))[:, cols]
+    check_gemm(y, y_ref, "gemm int5 long prefill")
+    check_gemv(y, y16, B16, "gemm int5 long prefill vs x16")
+
+
 def test_gemm_one_hot_selection_int5(torch):
     K, N = 256, 150
     w = _crafted(N, K, 5, (69,))
